@@ -1,0 +1,388 @@
+"""Pins for the CPU oracle: what the pages and mathematics fix, not the oracle.
+
+Page: "AVSG: Accelerated Vectorized Sparse Gather for Efficient KV Cache
+Offload in Sparse-Attention LLM Serving" (sections named per test), and
+"PulseInfer: I/O-Centric Sparse KV Cache Offloading" (recall as a set
+difference of the selected blocks and the GPU-resident blocks).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import Oracle, rates
+from workloads import gen_fuzz, make
+
+from _ref import BruteState, DictSim, as_np_state, brute_step
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _oracle(B=1, Nq=1, K=4, S=8, L=2, R=1, a1=1, a2=1, afp=1 << 17,
+            row_bytes=16, host_rows_total=None, host_rows=100):
+    return Oracle(B, Nq, K, S, L, R, a1, a2, afp, row_bytes,
+                  host_rows_total if host_rows_total is not None else B * host_rows)
+
+
+def _step(o, topk, ctx, host_rows=100):
+    B = o.B
+    return o.step(np.asarray(topk, np.int32).reshape(B, o.Nq, o.K),
+                  np.full(B, ctx, np.int32) if np.isscalar(ctx) else ctx,
+                  np.arange(B, dtype=np.int64) * host_rows,
+                  np.full(B, host_rows, np.int32))
+
+
+# ------------------------------------------------------------- hash layer --
+
+@pytest.mark.parametrize("S", [16, 64, 512, 8192])
+def test_probe_sequence_is_a_permutation_when_R_is_S_minus_1(S):
+    """Odd stride mod a power of two visits every bucket once (section 3.3:
+    strides are forced odd); so with R = S-1 no probe can miss a reusable
+    bucket."""
+    rng = np.random.default_rng(S)
+    for _ in range(5):
+        a1, a2 = (int(v) * 2 + 1 for v in rng.integers(0, 2**31, 2))
+        o = Oracle(1, 1, 1, S, 3, S - 1, a1, a2, 12345, 16, 1 << 20)
+        for x in rng.integers(0, 1 << 30, 8):
+            seq = o.probe_buckets(int(x))
+            assert sorted(seq) == list(range(S))
+
+
+def test_probe_home_and_stride_match_exact_integer_arithmetic():
+    """h = (a1 x) mod S and d = ((a2 x) mod S) | 1 (section 3.3), checked
+    against unbounded-integer arithmetic for ids near 2^31 where the 32-bit
+    products wrap."""
+    S, R = 4096, 3
+    a1, a2 = 0x9E3779B1, 0x85EBCA77
+    o = Oracle(1, 1, 1, S, 3, R, a1, a2, 1, 16, 1 << 31)
+    for x in [0, 1, 7, 4095, 4096, 123456789, 2**31 - 1, 2**31 - 4097]:
+        h, d = (a1 * x) % S, ((a2 * x) % S) | 1
+        assert o.probe_buckets(x) == [(h + t * d) % S for t in range(R + 1)]
+
+
+def test_word_packs_fingerprint_and_slot():
+    """One packed word holds a fingerprint and a destination slot (App. B,
+    "Collision and probe-budget semantics")."""
+    o = Oracle(1, 1, 1, 64, 3, 3, 1, 1, 0xC2B2AE3D, 16, 100)
+    for x, s in [(0, 0), (5, 63), (2**31 - 1, 17), (99999, 1)]:
+        w = o.word(x, s)
+        assert w >= 0 and w & 0xFFFF == s
+        assert w >> 16 == ((x * 0xC2B2AE3D) % 2**32) >> 17
+
+
+# ------------------------------------------------------ hand-worked case --
+
+def test_handworked_s8_example():
+    """A four-step case worked by hand from the page's rules (derivations in
+    the fixture): a lost collision, an exhausted probe, invalidation of ids
+    beyond the verified length, and an extra decay with live evictions."""
+    with open(os.path.join(GOLDEN, "handworked_s8.json")) as f:
+        case = json.load(f)
+    p = case["params"]
+    o = Oracle(p["B"], p["Nq"], p["K"], p["S"], p["L"], p["R"], p["a1"],
+               p["a2"], p["afp"], p["row_bytes"], case["host_rows"])
+    for st in case["steps"]:
+        out = _step(o, st["topk"], st["ctx_len"], case["host_rows"])
+        assert out.slot_table.ravel().tolist() == st["slot_table"]
+        assert out.hit_mask.ravel().tolist() == st["hit_mask"]
+        assert int(out.n_miss[0, 0]) == st["n_miss"]
+        n = st["n_miss"]
+        assert out.miss_pairs[0, 0, :n].tolist() == st["miss_pairs"]
+        assert o.Q[0].tolist() == st["Q"]
+        assert o.C[0].tolist() == st["C"]
+        assert o.F[0].tolist() == st["F"]
+        assert o.CNT[0].tolist() == st["CNT"]
+
+
+# ----------------------------------------------------------- closed forms --
+
+def test_disjoint_full_selections_map_rank_to_slot():
+    """K = S and every step selects S fresh ids: everything misses, the extra
+    decay reaches L, and the r-th smallest id lands in slot r (section 3.3
+    allocation; misses ascending, lowest dead slots first)."""
+    S, L = 64, 3
+    o = Oracle(1, 1, S, S, L, 7, 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D, 16, 1 << 20)
+    rng = np.random.default_rng(1)
+    pool = rng.permutation(1 << 20)
+    for t in range(5):
+        X = pool[t * S:(t + 1) * S].astype(np.int32)
+        out = _step(o, X, 1 << 20, 1 << 20)
+        rank = np.argsort(np.argsort(X))
+        assert (out.hit_mask == 0).all()
+        assert out.slot_table.ravel().tolist() == rank.tolist()
+        assert o.C[0].tolist() == sorted(X.tolist())
+        assert (o.F[0] == L).all()
+        if t > 0:
+            assert int(o.CNT[0, oracle.LIVE_EVICTIONS]) == t * S
+
+
+def test_repeated_selection_hits_everything_after_first_step():
+    """Ids with distinct residues mod S never share a home bucket, so nothing
+    is lost; repeating one selection then hits every id in its slot
+    (section 3.1 hit definition; section 3.5 refresh keeps them alive)."""
+    S, K = 256, 96
+    rng = np.random.default_rng(2)
+    X = (rng.permutation(S)[:K] + S * rng.integers(0, 50, K)).astype(np.int32)
+    o = Oracle(1, 1, K, S, 2, 3, 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D, 16, 50 * S)
+    first = _step(o, X, 50 * S, 50 * S)
+    assert (first.hit_mask == 0).all()
+    assert int(o.CNT[0, oracle.LOST_COLLISION]) == 0
+    for _ in range(6):
+        out = _step(o, X, 50 * S, 50 * S)
+        assert (out.hit_mask == 1).all()
+        assert (out.slot_table == first.slot_table).all()
+        assert int(out.n_miss.sum()) == 0
+
+
+@pytest.mark.parametrize("Nq", [2, 4])
+def test_mtp_identical_tokens_reuse_closed_form(Nq):
+    """From an empty buffer, N_q tokens that select the same ids share one
+    reservation: reuse = (N_q - 1) / N_q exactly (section 3.6 progressive
+    reuse; 4 tokens give 3/4)."""
+    S, K = 512, 128
+    X = (np.arange(K) * 3).astype(np.int32)
+    o = Oracle(1, Nq, K, S, 4, 7, 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D, 16, 4096)
+    out = o.step(np.tile(X, (1, Nq, 1)), np.array([4096], np.int32),
+                 np.zeros(1, np.int64), np.array([4096], np.int32))
+    assert int(out.n_miss[0, 0]) == K and int(out.n_miss[0, 1:].sum()) == 0
+    hits, lookups = int(o.CNT[0, oracle.HITS]), int(o.CNT[0, oracle.LOOKUPS])
+    copies = int(out.n_miss.sum())
+    assert rates.reuse_rate(copies, lookups) == pytest.approx((Nq - 1) / Nq, abs=0)
+    assert rates.hit_rate(hits, lookups) == pytest.approx((Nq - 1) / Nq, abs=0)
+    for g in range(1, Nq):
+        assert (out.slot_table[0, g] == out.slot_table[0, 0]).all()
+
+
+def test_speculative_ids_miss_on_the_next_step():
+    """Ids at or beyond the verified length N are emptied at end of step, so
+    reselecting them misses and copies again (App. B, Speculative
+    Invalidation; section 3.6)."""
+    S, K = 64, 8
+    o = _oracle(K=K, S=S, L=5, R=7, a1=0x9E3779B1, a2=0x85EBCA77, afp=0xC2B2AE3D)
+    X = np.array([1, 2, 3, 40, 41, 42, 43, 44], np.int32)
+    _step(o, X, 40)
+    assert set(o.C[0][o.C[0] >= 0].tolist()) == {1, 2, 3}
+    out = _step(o, X, 40)
+    assert out.hit_mask.ravel().tolist() == [1, 1, 1, 0, 0, 0, 0, 0]
+
+
+def test_padding_and_out_of_range_ids():
+    """-1 is padding (slot -1, mask -1); other out-of-range ids are padding too
+    and raise the sticky error bit; nothing else changes."""
+    o = _oracle(K=6, S=16, R=3)
+    out = _step(o, [5, -1, -7, 100, 101, 6], 100)
+    assert out.slot_table.ravel().tolist()[1:5] == [-1] * 4
+    assert out.hit_mask.ravel().tolist() == [0, -1, -1, -1, -1, 0]
+    assert int(o.CNT[0, oracle.ERRORS]) == oracle.ERR_OUT_OF_RANGE
+    assert int(o.CNT[0, oracle.LOOKUPS]) == 2
+
+
+def test_request_with_rows_outside_pool_is_all_padding():
+    o = Oracle(2, 1, 3, 16, 2, 3, 1, 1, 1 << 17, 16, 150)
+    out = o.step(np.array([[[1, 2, 3]], [[1, 2, 3]]], np.int32),
+                 np.array([100, 100], np.int32), np.array([0, 100], np.int64),
+                 np.array([100, 100], np.int32))
+    assert (out.hit_mask[0] == 0).all() and (out.hit_mask[1] == -1).all()
+    assert o.CNT[:, oracle.ERRORS].tolist() == [0, 1]
+
+
+def test_duplicate_ids_flagged_and_kept_separate():
+    o = _oracle(K=4, S=16, R=3)
+    out = _step(o, [9, 9, 3, -1], 100)
+    assert int(o.CNT[0, oracle.ERRORS]) & oracle.ERR_DUPLICATE
+    s = out.slot_table.ravel().tolist()
+    assert s[0] != s[1] and min(s[:3]) >= 0
+
+
+def test_lifetime_survives_L_decays_then_dies():
+    """A slot set to L stays reusable-protected for L unit decays and is
+    reclaimable after L+1 (section 3.5; App. B slot preservation)."""
+    L = 3
+    o = _oracle(K=1, S=16, L=L, R=3)
+    _step(o, [7], 100)
+    slot = int(np.flatnonzero(o.C[0] == 7)[0])
+    for k in range(1, L + 1):
+        _step(o, [-1], 100)
+        assert o.F[0, slot] == L - k
+    _step(o, [-1], 100)
+    assert o.F[0, slot] == -1
+
+
+# -------------------------------------------------- brute force and sims --
+
+def _fuzz_cases(n):
+    return [gen_fuzz(s) for s in range(n)]
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_oracle_matches_brute_force_transcription(chunk):
+    """Every output and state entry agrees with the literal transcription on
+    a fuzz corpus covering padding, out-of-range and speculative ids, MTP,
+    R in {0, 1, 3, S-1} and L in {1, 2, 3, 5}."""
+    for w in _fuzz_cases(400)[chunk::4]:
+        o = Oracle.for_workload(w)
+        st = BruteState(w.B, w.S)
+        p = w.params()
+        for t in range(w.steps):
+            out = o.step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
+            O, H, n, pairs = brute_step(st, p, w.topk[t].tolist(), w.ctx_len[t].tolist(),
+                                        w.row_base.tolist(), w.host_rows.tolist(),
+                                        w.host_rows_total)
+            Q, C, F, CNT = as_np_state(st)
+            ctx = f"{w.name} step {t}"
+            assert out.slot_table.tolist() == O, ctx
+            assert out.hit_mask.tolist() == H, ctx
+            assert out.n_miss.tolist() == n, ctx
+            for b in range(w.B):
+                for g in range(w.Nq):
+                    assert out.miss_pairs[b, g, :n[b][g]].tolist() == [list(x) for x in pairs[b][g]], ctx
+            assert (o.Q == Q).all() and (o.C == C).all() and (o.F == F).all(), ctx
+            assert (o.CNT.astype(np.int64) == CNT).all(), ctx
+
+
+def test_oracle_matches_dictionary_simulator_while_nothing_is_lost():
+    """While no bucket mapping has been lost, the hash table is an exact
+    dictionary of the cached ids, so the oracle must equal an LRU-with-aging
+    simulator that has no hash table at all (section 3.5 aging; section 3.3
+    allocation)."""
+    compared = evictions = 0
+    for seed in range(300):
+        rng = np.random.default_rng([11, seed])
+        S = int(rng.choice([32, 64]))
+        Nq = int(rng.integers(1, 3))
+        K = int(rng.integers(2, 9))
+        L = int(rng.choice([1, 2, 3]))
+        univ = int(rng.integers(2 * K, 4 * S))
+        o = Oracle(1, Nq, K, S, L, S - 1, int(rng.integers(0, 2**31)) * 2 + 1,
+                   int(rng.integers(0, 2**31)) * 2 + 1, 0xC2B2AE3D, 16, univ)
+        sim = DictSim(S, L)
+        for t in range(12):
+            N = int(rng.integers(univ // 2, univ + 1))
+            toks = [rng.choice(univ, K, replace=False).astype(np.int32) for _ in range(Nq)]
+            before = o.CNT[0, oracle.LOST_COLLISION] + o.CNT[0, oracle.LOST_EXHAUSTED]
+            out = o.step(np.array(toks)[None], np.array([N], np.int32),
+                         np.zeros(1, np.int64), np.array([univ], np.int32))
+            lost = o.CNT[0, oracle.LOST_COLLISION] + o.CNT[0, oracle.LOST_EXHAUSTED]
+            res = sim.step([tk.tolist() for tk in toks], N)
+            if before != 0 or (Nq > 1 and lost != 0):
+                break
+            # With one token, slots and hit flags are decided before the
+            # step's link writes, so they agree even if the step loses a
+            # mapping; with several tokens a loss can change later tokens.
+            for g in range(Nq):
+                for i, x in enumerate(toks[g].tolist()):
+                    assert (int(out.slot_table[0, g, i]), int(out.hit_mask[0, g, i])) == res[g][x]
+            assert o.C[0].tolist() == sim.C and o.F[0].tolist() == sim.F
+            assert int(o.CNT[0, oracle.LIVE_EVICTIONS]) == sim.live_evictions
+            compared += 1
+            evictions = max(evictions, sim.live_evictions)
+            if lost != 0:
+                break
+    assert compared > 1000 and evictions > 0
+
+
+def test_hits_are_the_set_intersection_with_resident_ids():
+    """Recall = selected \\ resident (PulseInfer page, recall stage): while
+    nothing is lost, the hits of a single-token step are exactly the selected
+    ids that the buffer caches before the step."""
+    S, K = 1024, 24
+    checked = 0
+    for seed in range(40):
+        rng = np.random.default_rng([5, seed])
+        o = Oracle(1, 1, K, S, 4, S - 1, 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D, 16, 600)
+        for t in range(40):
+            resident = set(o.C[0][o.C[0] >= 0].tolist())
+            X = rng.choice(600, K, replace=False).astype(np.int32)
+            if int(o.CNT[0, 3] + o.CNT[0, 4]):
+                break
+            out = _step(o, X, 600, 600)
+            hits = {int(x) for x, h in zip(X, out.hit_mask.ravel()) if h == 1}
+            assert hits == set(X.tolist()) & resident
+            assert {int(x) for x, h in zip(X, out.hit_mask.ravel()) if h == 0} == \
+                set(X.tolist()) - resident
+            checked += 1
+    assert checked > 150
+
+
+# ------------------------------------------------------------- invariants --
+
+@pytest.mark.parametrize("name", ["tiny", "mtp3"])
+def test_invariants_on_workloads(name):
+    """After every step: every valid, non-speculative id's slot caches it
+    (slots referenced earlier in a request survive the step, App. B slot
+    preservation), slots are distinct within a token, lifetimes stay in
+    [-1, L], hits + misses = valid lookups, and no hit has C[s] != x."""
+    w = make(name) if name == "tiny" else make(name, steps=3, B=2)
+    o = Oracle.for_workload(w)
+    for t in range(w.steps):
+        out = o.step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
+        for b in range(w.B):
+            for g in range(w.Nq):
+                X = w.topk[t, b, g]
+                v = X >= 0
+                s = out.slot_table[b, g][v]
+                assert len(set(s.tolist())) == s.size
+                keep = X[v] < w.ctx_len[t, b]
+                assert (o.C[b][s[keep]] == X[v][keep]).all()
+                assert (o.C[b][s[~keep]] == -1).all()
+        assert o.F.min() >= -1 and o.F.max() <= w.L
+        c = o.CNT.astype(np.int64)
+        assert (c[:, oracle.HITS] + c[:, oracle.MISSES] == c[:, oracle.LOOKUPS]).all()
+
+
+def test_capacity_bound_is_enforced():
+    """N_q * K <= S is the capacity bound of App. B; the oracle refuses more."""
+    o = Oracle(1, 2, 5, 8, 2, 1, 1, 1, 1, 16, 100)
+    with pytest.raises(oracle.OracleError):
+        o.step(np.zeros((1, 2, 5), np.int32), np.array([100], np.int32),
+               np.zeros(1, np.int64), np.array([100], np.int32))
+
+
+# ------------------------------------------------------------ data layer --
+
+def test_gathered_rows_equal_host_rows_of_cached_ids():
+    """After the copy, every slot a valid non-speculative id maps to holds that
+    id's host row (section 3.4) -- true for any correct tie-breaking."""
+    w = make("tiny")
+    host = np.empty(w.host_bytes, np.uint8)
+    w.fill_host_kv(host)
+    o = Oracle.for_workload(w, host_kv=host)
+    rows = host.reshape(-1, w.row_bytes)
+    for t in range(w.steps):
+        out = o.step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
+        X = w.topk[t, 0, 0]
+        s = out.slot_table[0, 0]
+        assert (o.shadow[0][s] == rows[w.row_base[0] + X]).all()
+
+
+# ---------------------------------------------------------- printed rates --
+
+def _golden_figures():
+    rows = {}
+    with open(os.path.join(GOLDEN, "paper_figures.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, inp, res, _ = [x.strip() for x in line.split("|")]
+                kv = dict(tok.split("=") for tok in (inp + " " + res).split())
+                rows[name] = {k: float(v) for k, v in kv.items()}
+    return rows
+
+
+def test_rate_definitions_reproduce_printed_figures():
+    g = _golden_figures()
+    m = g["mtp3_copies"]
+    assert round(rates.copies_at_reuse(m["lookups"], m["reuse"])) == m["copies"]
+    assert rates.reuse_rate(m["copies"], m["lookups"]) == pytest.approx(m["reuse"], abs=5e-5)
+    gg = g["gain_8k"]
+    assert round(rates.gain_pp(gg["hit_rate_pct"], gg["adjacent_pct"]), 2) == gg["gain_pp"]
+    ml = g["matching_latency"]
+    assert round(rates.latency_reduction(ml["before_us"], ml["after_us"]), 3) == ml["reduction"]
+    tp = g["tpot"]
+    # 1 - 55/91 = 39.6 %; the page prints the whole percent, 39 %.
+    assert int(100 * rates.latency_reduction(tp["kv_offload_ms"], tp["avsg_ms"])) == \
+        round(100 * tp["reduction"])
+    assert rates.adjacent_reuse([1, 2, 3, 4], [3, 4, 5, 6]) == 0.5

@@ -1,0 +1,381 @@
+"""Seeded synthetic inputs for the per-decode-step KV recall path.
+
+This module only *draws inputs*: the top-K token indices each query token
+selects, the verified context length of each request, where each request's
+rows sit in the host KV pool, and the bytes of that pool.  It holds none of
+the recall method's arithmetic (no hashing, probing, aging or slot choice),
+which is why both the CPU oracle and the GPU path may read from it.
+
+The pages measure on production agent requests, the ServeGen / Mooncake
+traces and real model weights, none of which are available here.  These
+generators stand in for them with the shapes the pages describe: a sparse
+indexer picks K = 2048 earlier tokens per query token (AVSG page, section 1
+and section 2 on DSA), selections drift between adjacent decode steps
+(AVSG page, section 4.4), MTP iterations carry one initial and several
+speculative tokens (AVSG page, section 3.6), and request lengths are
+long-tailed (PulseInfer page, section 3.3 on request-length CDFs).
+
+Every generator is a pure function of its seed: ``numpy.random.default_rng``
+seeded with ``[config_seed, request]`` per request, so requests can be drawn
+independently and in any order.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# Hash constants handed to both sides as plain configuration values.  The
+# pages do not print them (AVSG page, section 3.3, "Probe primitive"); any odd
+# 32-bit values are admissible.
+DEFAULT_A1 = 0x9E3779B1
+DEFAULT_A2 = 0x85EBCA77
+DEFAULT_AFP = 0xC2B2AE3D
+DEFAULT_L = 15
+DEFAULT_R = 7
+
+CONFIG_NAMES = ("tiny", "matching", "residency", "mtp3", "imbalanced")
+CONFIG_SEEDS = {"tiny": 101, "matching": 202, "residency": 303, "mtp3": 404,
+                "imbalanced": 505}
+
+_KV_CHUNK = 64 << 20  # host KV bytes are drawn in independent 64 MiB chunks
+
+
+@dataclass
+class Workload:
+    """One synthetic recall workload: shapes plus every step's inputs.
+
+    topk      int32 [steps][B][Nq][K]   selected token ids, -1 = padding
+    ctx_len   int32 [steps][B]          verified context length N per request
+    host_rows int32 [B]                 valid host rows of each request
+    row_base  int64 [B]                 first host row of each request
+    """
+    name: str
+    B: int
+    Nq: int
+    K: int
+    S: int
+    row_bytes: int
+    steps: int
+    seed: int
+    topk: np.ndarray
+    ctx_len: np.ndarray
+    host_rows: np.ndarray
+    row_base: np.ndarray
+    L: int = DEFAULT_L
+    R: int = DEFAULT_R
+    a1: int = DEFAULT_A1
+    a2: int = DEFAULT_A2
+    afp: int = DEFAULT_AFP
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def host_rows_total(self) -> int:
+        return int(self.row_base[-1] + self.host_rows[-1]) if self.B else 0
+
+    @property
+    def host_bytes(self) -> int:
+        return self.host_rows_total * self.row_bytes
+
+    @property
+    def lookups_per_step(self) -> int:
+        return self.B * self.Nq * self.K
+
+    def params(self) -> dict:
+        return dict(B=self.B, Nq=self.Nq, K=self.K, S=self.S, L=self.L,
+                    R=self.R, a1=self.a1, a2=self.a2, afp=self.afp,
+                    row_bytes=self.row_bytes)
+
+    def fill_host_kv(self, out: np.ndarray) -> None:
+        """Fill ``out`` (uint8, host_bytes long) with the pool's bytes."""
+        fill_random_bytes(out, self.seed)
+
+
+def fill_random_bytes(out: np.ndarray, seed: int) -> None:
+    """Uniform random bytes, drawn chunk by chunk from ``[seed, 9999, chunk]``."""
+    flat = out.reshape(-1)
+    assert flat.dtype == np.uint8
+    n = flat.size
+    for c, lo in enumerate(range(0, n, _KV_CHUNK)):
+        hi = min(n, lo + _KV_CHUNK)
+        rng = np.random.default_rng([seed, 9999, c])
+        flat[lo:hi] = np.frombuffer(rng.bytes(hi - lo), dtype=np.uint8)
+
+
+# ---------------------------------------------------------------- helpers --
+
+def _take_distinct(rng, need, draw, taken):
+    """Collect ``need`` distinct ids from ``draw(size)``, skipping ``taken``.
+
+    ``taken`` is a boolean mask over the id domain; accepted ids are marked in
+    it.  Ids are accepted in the order they are drawn.
+    """
+    got = []
+    have = 0
+    while have < need:
+        cand = draw(max(2 * (need - have), 256))
+        cand = cand[~taken[cand]]
+        if cand.size == 0:
+            continue
+        _, first = np.unique(cand, return_index=True)
+        cand = cand[np.sort(first)][: need - have]
+        taken[cand] = True
+        got.append(cand)
+        have += cand.size
+    return np.concatenate(got).astype(np.int64) if got else np.zeros(0, np.int64)
+
+
+def _zipf_sampler(rng, perm, s=1.1):
+    """Ids = perm[rank-1] with rank ~ Zipf(s), ranks beyond len(perm) rejected."""
+    limit = perm.size
+
+    def draw(size):
+        r = rng.zipf(s, size=size)
+        r = r[r <= limit]
+        return perm[r - 1]
+    return draw
+
+
+def _uniform_sampler(rng, hi):
+    def draw(size):
+        return rng.integers(0, hi, size=size)
+    return draw
+
+
+def _as_row(ids, K):
+    out = np.full(K, -1, np.int32)
+    out[: ids.size] = ids
+    return out
+
+
+# ------------------------------------------------------------ the configs --
+
+def gen_tiny(steps=16):
+    """1 request, context 4096, K=256, S=512, 1152-B rows (576 bf16).
+
+    Step 0 draws 256 distinct ids uniformly from [0, 4096).  Each later step
+    keeps round(0.7*256) = 179 of the previous ids, chosen uniformly, and adds
+    77 new distinct ids drawn uniformly from [0, 4096) minus the kept ones.
+    Ids are emitted sorted ascending.
+    """
+    seed, ctx, K = CONFIG_SEEDS["tiny"], 4096, 256
+    B, Nq = 1, 1
+    keep = int(round(0.7 * K))
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b])
+        prev = None
+        for t in range(steps):
+            if prev is None:
+                ids = rng.choice(ctx, K, replace=False)
+            else:
+                kept = rng.choice(prev, keep, replace=False)
+                taken = np.zeros(ctx, bool)
+                taken[kept] = True
+                new = _take_distinct(rng, K - keep, _uniform_sampler(rng, ctx), taken)
+                ids = np.concatenate([kept, new])
+            ids = np.sort(ids)
+            topk[t, b, 0] = ids
+            prev = ids
+    return Workload("tiny", B, Nq, K, 512, 1152, steps, seed, topk,
+                    np.full((steps, B), ctx, np.int32), np.full(B, ctx, np.int32),
+                    np.arange(B, dtype=np.int64) * ctx)
+
+
+def _window_plus_zipf(rng, perm, ctx, K, win):
+    window = np.arange(ctx - win, ctx)
+    taken = np.zeros(ctx, bool)
+    taken[window] = True
+    z = _take_distinct(rng, K - win, _zipf_sampler(rng, perm), taken)
+    return window, z
+
+
+def gen_matching(steps=64):
+    """Batch 8, context 65536, K=2048, S=2048, 1280-B rows (576 bf16 + 128 fp8).
+
+    Every step selects the 256-token recency window [ctx-256, ctx) plus 1792
+    distinct ids whose Zipf(s=1.1) ranks are mapped through a per-request
+    random permutation of [0, ctx-256) (fixed per request, so low ranks form
+    a hot set); the Zipf draws are redrawn every step.  Ids are emitted in
+    random order.
+    """
+    seed, ctx, K, win = CONFIG_SEEDS["matching"], 65536, 2048, 256
+    B, Nq = 8, 1
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b])
+        perm = rng.permutation(ctx - win)
+        for t in range(steps):
+            window, z = _window_plus_zipf(rng, perm, ctx, K, win)
+            topk[t, b, 0] = rng.permutation(np.concatenate([window, z]))
+    return Workload("matching", B, Nq, K, 2048, 1280, steps, seed, topk,
+                    np.full((steps, B), ctx, np.int32), np.full(B, ctx, np.int32),
+                    np.arange(B, dtype=np.int64) * ctx)
+
+
+def gen_residency(steps=128, B=32):
+    """Batch 32, context 131072, K=2048, S=8192, 1280-B rows, 15 % drift.
+
+    Step 0 is drawn as in the matching workload.  Each later step keeps the
+    recency window, keeps 1792-307 = 1485 of the previous step's non-window
+    ids (uniformly chosen) and replaces round(0.15*2048) = 307 of them with
+    fresh Zipf draws not already selected, so adjacent-step reuse is about
+    85 % by construction.  Ids are emitted in random order.
+    """
+    seed, ctx, K, win = CONFIG_SEEDS["residency"], 131072, 2048, 256
+    Nq = 1
+    repl = int(round(0.15 * K))
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b])
+        perm = rng.permutation(ctx - win)
+        window, z = _window_plus_zipf(rng, perm, ctx, K, win)
+        for t in range(steps):
+            if t > 0:
+                kept = rng.choice(z, z.size - repl, replace=False)
+                taken = np.zeros(ctx, bool)
+                taken[window] = True
+                taken[kept] = True
+                fresh = _take_distinct(rng, repl, _zipf_sampler(rng, perm), taken)
+                z = np.concatenate([kept, fresh])
+            topk[t, b, 0] = rng.permutation(np.concatenate([window, z]))
+    return Workload("residency", B, Nq, K, 8192, 1280, steps, seed, topk,
+                    np.full((steps, B), ctx, np.int32), np.full(B, ctx, np.int32),
+                    np.arange(B, dtype=np.int64) * ctx)
+
+
+def gen_mtp3(steps=32, B=16):
+    """Batch 16, 4 query tokens per iteration (1 initial + 3 speculative).
+
+    Iteration t has verified length N_t = 100000 - 128 + 4t.  Token g selects
+    the window [N_t+g-256, N_t+g) (so tokens g >= 1 also select the
+    speculative positions [N_t, N_t+g)).  Token 0 adds 1792 distinct Zipf ids
+    over a per-request permutation of [0, 99616); token g >= 1 keeps
+    round(0.6*1792) = 1075 of them (uniformly chosen) and adds 717 fresh Zipf
+    ids not among token 0's.  Host rows exist for all positions < 100000.
+    The buffer starts empty.
+    """
+    seed, ctx, K, win, Nq = CONFIG_SEEDS["mtp3"], 100000, 2048, 256, 4
+    base = ctx - 128
+    dom = base - win
+    n_z = K - win
+    keep = int(round(0.6 * n_z))
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    ctx_len = np.zeros((steps, B), np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b])
+        perm = rng.permutation(dom)
+        for t in range(steps):
+            N = base + 4 * t
+            ctx_len[t, b] = N
+            taken0 = np.zeros(dom, bool)
+            z0 = _take_distinct(rng, n_z, _zipf_sampler(rng, perm), taken0)
+            for g in range(Nq):
+                window = np.arange(N + g - win, N + g)
+                if g == 0:
+                    z = z0
+                else:
+                    kept = rng.choice(z0, keep, replace=False)
+                    taken = taken0.copy()
+                    fresh = _take_distinct(rng, n_z - keep, _zipf_sampler(rng, perm), taken)
+                    z = np.concatenate([kept, fresh])
+                topk[t, b, g] = rng.permutation(np.concatenate([window, z]))
+    return Workload("mtp3", B, Nq, K, 8192, 1280, steps, seed, topk, ctx_len,
+                    np.full(B, ctx, np.int32), np.arange(B, dtype=np.int64) * ctx)
+
+
+def gen_imbalanced(steps=64, B=64):
+    """64 requests with lognormal lengths, S=4096, 1280-B rows.
+
+    len_b = clip(round(16384 * exp(z_b)), 2048, 262144) with z_b ~ N(0, 1)
+    (median 16K); per-request drift r_b ~ U(0, 0.6).  K_b = min(2048, len_b)
+    = 2048.  Step 0 draws K distinct ids uniformly from [0, len_b); each later
+    step keeps round((1-r_b)*K) of the previous ids and draws the rest
+    uniformly from [0, len_b) minus the kept ones.  Host rows are packed:
+    row_base[b] = sum of earlier lengths.  Ids are emitted in random order.
+    """
+    seed, K = CONFIG_SEEDS["imbalanced"], 2048
+    Nq = 1
+    rl = np.random.default_rng([seed, 7777])
+    z = rl.standard_normal(B)
+    lens = np.clip(np.round(16384 * np.exp(z)), 2048, 262144).astype(np.int64)
+    drift = rl.uniform(0.0, 0.6, B)
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b])
+        n = int(lens[b])
+        kb = min(K, n)
+        keep = int(round((1.0 - drift[b]) * kb))
+        prev = None
+        for t in range(steps):
+            if prev is None:
+                ids = rng.choice(n, kb, replace=False)
+            else:
+                kept = rng.choice(prev, keep, replace=False)
+                taken = np.zeros(n, bool)
+                taken[kept] = True
+                new = _take_distinct(rng, kb - keep, _uniform_sampler(rng, n), taken)
+                ids = np.concatenate([kept, new])
+            ids = rng.permutation(ids)
+            topk[t, b, 0] = _as_row(ids, K)
+            prev = ids
+    row_base = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    ctx = np.broadcast_to(lens.astype(np.int32), (steps, B)).copy()
+    w = Workload("imbalanced", B, Nq, K, 4096, 1280, steps, seed, topk, ctx,
+                 lens.astype(np.int32), row_base)
+    w.extra["drift"] = drift
+    return w
+
+
+GENERATORS = {"tiny": gen_tiny, "matching": gen_matching,
+              "residency": gen_residency, "mtp3": gen_mtp3,
+              "imbalanced": gen_imbalanced}
+
+
+def make(name: str, **kw) -> Workload:
+    return GENERATORS[name](**kw)
+
+
+# ----------------------------------------------------------- fuzz corpus --
+
+def gen_fuzz(seed: int, steps: int = 6) -> Workload:
+    """A small random case: B<=3, Nq<=3, K<=16, S in {16, 32, 64}.
+
+    Ids come from a small universe so hits, evictions, lost mappings and
+    speculative ids all occur.  Padding (-1), out-of-range ids and ids beyond
+    the verified length are mixed in.  The capacity bound Nq*K <= S holds.
+    """
+    rng = np.random.default_rng([7, seed])
+    S = int(rng.choice([16, 32, 64]))
+    Nq = int(rng.integers(1, 4))
+    K = int(rng.integers(1, min(16, S // Nq) + 1))
+    B = int(rng.integers(1, 4))
+    L = int(rng.choice([1, 2, 3, 5]))
+    R = int(rng.choice([0, 1, 3, S - 1]))
+    univ = int(rng.integers(K + 1, 6 * S))
+    host_rows = rng.integers(max(1, univ // 2), univ + 1, size=B).astype(np.int32)
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    ctx = np.zeros((steps, B), np.int32)
+    for t in range(steps):
+        for b in range(B):
+            hr = int(host_rows[b])
+            ctx[t, b] = int(rng.integers(max(1, hr // 2), hr + 1))
+            for g in range(Nq):
+                n = int(rng.integers(0, min(K, hr) + 1))
+                ids = rng.choice(hr, n, replace=False).astype(np.int32)
+                row = np.full(K, -1, np.int32)
+                pos = rng.permutation(K)[:n]
+                row[pos] = ids
+                # occasionally plant an out-of-range id in a padding position
+                if n < K and rng.random() < 0.15:
+                    free = np.setdiff1d(np.arange(K), pos)
+                    row[free[0]] = int(rng.choice([-5, hr, hr + 3]))
+                topk[t, b, g] = row
+    row_base = np.concatenate([[0], np.cumsum(host_rows)[:-1]]).astype(np.int64)
+    a1 = int(rng.integers(0, 2**31)) * 2 + 1
+    a2 = int(rng.integers(0, 2**31)) * 2 + 1
+    afp = int(rng.integers(0, 2**31)) * 2 + 1
+    row_bytes = int(rng.choice([16, 32, 64]))
+    return Workload(f"fuzz{seed}", B, Nq, K, S, row_bytes, steps, 1000 + seed,
+                    topk, ctx, host_rows, row_base, L=L, R=R, a1=a1, a2=a2,
+                    afp=afp)
