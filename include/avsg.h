@@ -1,0 +1,210 @@
+/*
+ * avsg.h - C ABI of the per-decode-step KV recall library for MI355X (gfx950).
+ *
+ * The library makes the KV rows that a sparse-attention step selected
+ * resident in device memory.  For every request it matches the top-K
+ * selected token ids of each query token against a fixed-capacity slot
+ * buffer with an open-addressing hash probe, assigns the misses slots by
+ * per-slot aging with hit-triggered lifetime refresh, copies the missed rows
+ * from pinned host memory into their slots, and emits the slot table that
+ * attention reads.  The method is the one described on the page "AVSG:
+ * Accelerated Vectorized Sparse Gather for Efficient KV Cache Offload in
+ * Sparse-Attention LLM Serving" (cited below as AVSG with its section).
+ *
+ * Conventions
+ *  - Every function returns AVSG_OK (0) or a negative AVSG_E* code.  On
+ *    AVSG_EHIP, avsg_last_hip_error() returns the HIP error of the failing
+ *    call on this thread.
+ *  - "device" pointers are HIP device allocations on the device that was
+ *    current when avsg_create ran; "host" pointers are host memory.
+ *  - All buffers are caller-owned and must outlive the handle.  The library
+ *    owns only the handle and a workspace it allocates in avsg_create.
+ *  - avsg_match / avsg_gather / avsg_step only enqueue kernels on `stream`
+ *    (a hipStream_t; NULL = the null stream).  They never synchronise, never
+ *    allocate and never call hipMemset, so a step can be captured in a HIP
+ *    graph and replayed; each replay reads the io buffers at the addresses
+ *    given at capture time.
+ *  - Bad device data never faults: an id outside a request's host rows is
+ *    treated as padding and sets AVSG_ERR_OUT_OF_RANGE in that request's
+ *    error counter.
+ */
+#ifndef AVSG_H
+#define AVSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AVSG_VERSION 1
+
+/* Return codes. */
+#define AVSG_OK 0
+#define AVSG_EINVAL (-1)       /* bad argument or configuration */
+#define AVSG_ENOMEM (-2)       /* workspace allocation failed */
+#define AVSG_EHIP (-3)         /* a HIP runtime call failed */
+#define AVSG_EUNSUPPORTED (-4) /* valid for the method, beyond this build's
+                                  limits (e.g. state does not fit in LDS) */
+
+/* Per-request counters, CNT[b][0..7]; they accumulate over steps and wrap
+ * modulo 2^32.  Rates are derived from them by the caller (hit rate =
+ * HITS / LOOKUPS, AVSG s4.4). */
+#define AVSG_CNT_HITS 0            /* valid ids found in the buffer */
+#define AVSG_CNT_LOOKUPS 1         /* valid ids looked up */
+#define AVSG_CNT_MISSES 2          /* ids given a new slot (one copy each) */
+#define AVSG_CNT_LOST_COLLISION 3  /* links overwritten in the same scatter */
+#define AVSG_CNT_LOST_EXHAUSTED 4  /* links with no reusable bucket in R+1 */
+#define AVSG_CNT_LIVE_EVICTIONS 5  /* victim slots that still cached an id */
+#define AVSG_CNT_ERRORS 6          /* sticky AVSG_ERR_* bits */
+#define AVSG_CNT_PROBE_VISITS 7    /* buckets examined: t+1 per hit found in
+                                      round t, R+1 per miss */
+
+#define AVSG_ERR_OUT_OF_RANGE 1u   /* id not -1 and outside [0, host_rows[b]),
+                                      or the request's rows leave the pool */
+#define AVSG_ERR_DUPLICATE 2u      /* one token missed the same id twice */
+
+/* Config flags. */
+#define AVSG_FLAG_SKIP_GATHER 1u   /* avsg_step runs Stage One only (no host
+                                      pool needed) */
+
+typedef struct avsg_config {
+    int32_t B;         /* requests (batch rows), >= 1 */
+    int32_t N_q;       /* query tokens per request and step: 1 initial plus
+                          N_mtp speculative ones, processed in order through
+                          one shared buffer (AVSG s3.6), >= 1 */
+    int32_t K;         /* selected ids per query token, 1..8192 */
+    int32_t S;         /* slots (and hash buckets) per request: a power of
+                          two, 16..65536, with N_q*K <= S (capacity bound,
+                          AVSG App. B "Slot preservation") */
+    int32_t L;         /* lifetime given on refresh or install, 1..127
+                          (AVSG s3.5) */
+    int32_t R;         /* probe rounds beyond the first: a lookup examines up
+                          to R+1 buckets (AVSG s3.3 "Probe primitive"), >= 0 */
+    uint32_t a1;       /* odd multiplier of the home bucket (a1*x) mod S */
+    uint32_t a2;       /* odd multiplier of the stride ((a2*x) mod S) | 1 */
+    uint32_t a_fp;     /* odd multiplier of the 15-bit fingerprint
+                          (x*a_fp mod 2^32) >> 17 kept in bucket words */
+    int32_t row_bytes; /* bytes per KV row (e.g. 576 bf16 latent + 128 fp8
+                          indexer key = 1280), a positive multiple of 16 */
+    uint32_t flags;    /* AVSG_FLAG_* */
+    int32_t gather_blocks; /* Stage-Two workgroups; 0 = chosen from the CU
+                              count */
+} avsg_config;
+
+/* Caller-owned buffers bound at create time. */
+typedef struct avsg_buffers {
+    int32_t* Q;        /* device int32 [B][S]: bucket words fp<<16 | slot,
+                          -1 = empty */
+    int32_t* C;        /* device int32 [B][S]: cached token id per slot,
+                          -1 = empty */
+    int32_t* F;        /* device int32 [B][S]: lifetime per slot, -1 = dead,
+                          else 0..L */
+    int32_t* CNT;      /* device int32 [B][8]: AVSG_CNT_* counters */
+    void* dev_kv;      /* device bytes [B][S][row_bytes]: the slot buffer
+                          attention reads; slot s of request b is row b*S+s */
+    const void* host_kv; /* pinned host bytes [host_rows_total][row_bytes]
+                          (from avsg_host_alloc or any pinned, device-mapped
+                          allocation); may be NULL with AVSG_FLAG_SKIP_GATHER */
+    int64_t host_rows_total; /* rows in host_kv */
+} avsg_buffers;
+
+/* Per-step inputs and outputs: device pointers. */
+typedef struct avsg_step_io {
+    const int32_t* topk;      /* int32 [B][N_q][K]: selected ids, any order,
+                                 -1 = padding; ids of one token are expected
+                                 distinct (AVSG_ERR_DUPLICATE otherwise) */
+    const int32_t* ctx_len;   /* int32 [B]: verified context length N; ids
+                                 >= N are speculative and their slots are
+                                 emptied at the end of the step (AVSG App. B,
+                                 "Speculative Invalidation") */
+    const int64_t* row_base;  /* int64 [B]: host row of token 0 of request b */
+    const int32_t* host_rows; /* int32 [B]: valid host rows of request b */
+    int32_t* slot_table;      /* out int32 [B][N_q][K]: slot in [0, S) of each
+                                 valid id, -1 for padding (AVSG s3.3: device
+                                 positions for attention) */
+    int8_t* hit_mask;         /* out int8 [B][N_q][K]: 1 hit, 0 miss,
+                                 -1 padding */
+    int32_t* n_miss;          /* out int32 [B][N_q]: misses of each token
+                                 (the vector n of AVSG s3.3/s3.4) */
+    int32_t* miss_pairs;      /* out int32 [B][N_q][K][2] or NULL: entry r of
+                                 token (b,g) holds (id, slot) of its r-th
+                                 smallest missing id for r < n_miss; NULL uses
+                                 the library's workspace */
+} avsg_step_io;
+
+typedef struct avsg_handle avsg_handle;
+
+int avsg_version(void);
+
+/* Static text for a return code. */
+const char* avsg_strerror(int code);
+
+/* HIP error code (hipError_t value) of the last failing HIP call made by
+ * this library on the calling thread; 0 if none. */
+int avsg_last_hip_error(void);
+
+/* Fill cfg with the given shape and the defaults L = 15, R = 7,
+ * a1 = 0x9E3779B1, a2 = 0x85EBCA77, a_fp = 0xC2B2AE3D, flags = 0,
+ * gather_blocks = 0. */
+void avsg_config_default(avsg_config* cfg, int32_t B, int32_t N_q, int32_t K,
+                         int32_t S, int32_t row_bytes);
+
+/* AVSG_OK if cfg satisfies every constraint documented in avsg_config,
+ * AVSG_EINVAL otherwise.  Needs no GPU. */
+int avsg_validate_config(const avsg_config* cfg);
+
+/* LDS bytes the Stage-One kernel needs for cfg (one workgroup holds one
+ * request's bucket words, ids and lifetimes).  avsg_create returns
+ * AVSG_EUNSUPPORTED if this exceeds the device's per-workgroup LDS.  Needs
+ * no GPU. */
+size_t avsg_stage1_lds_bytes(const avsg_config* cfg);
+
+/* Device bytes avsg_create allocates for its workspace.  Needs no GPU. */
+size_t avsg_workspace_bytes(const avsg_config* cfg);
+
+/* Validate cfg and bufs, resolve the device alias of host_kv, allocate the
+ * workspace and return a handle in *out.  Enqueues no work; the state
+ * buffers must be initialised with avsg_state_init before the first step.
+ * On failure *out is NULL and nothing is leaked. */
+int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs,
+                avsg_handle** out);
+
+/* Free the handle and its workspace (not the caller's buffers).  NULL is
+ * accepted.  Work already enqueued must have finished. */
+int avsg_destroy(avsg_handle* h);
+
+/* Enqueue a reset of request rows to the empty state: Q = C = F = -1,
+ * CNT = 0.  row_mask: device int32 [B], nonzero = reset that row; NULL =
+ * all rows.  Uses a kernel (no hipMemset). */
+int avsg_state_init(avsg_handle* h, const int32_t* row_mask, void* stream);
+
+/* Stage One (AVSG s3.3, s3.5, s3.6 and App. B): for every request, pre-decay
+ * lifetimes, then for each query token in order probe, refresh hits, classify,
+ * choose victims, install misses and link bucket words; finally empty the
+ * slots of speculative ids.  Writes slot_table, hit_mask, n_miss, the miss
+ * list, and updates Q, C, F, CNT. */
+int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream);
+
+/* Stage Two (AVSG s3.4): copy the host row of every miss listed by the last
+ * avsg_match on this io into its slot of dev_kv, with the missed rows split
+ * evenly across workgroups by flat miss index (not by request).  Reads
+ * n_miss, the miss list and row_base.  AVSG_EINVAL if host_kv is NULL. */
+int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream);
+
+/* avsg_match followed by avsg_gather (the gather is skipped under
+ * AVSG_FLAG_SKIP_GATHER). */
+int avsg_step(avsg_handle* h, const avsg_step_io* io, void* stream);
+
+/* Allocate `bytes` of pinned host memory mapped into the device's address
+ * space, suitable as host_kv; *out = host address.  Free with
+ * avsg_host_free. */
+int avsg_host_alloc(size_t bytes, void** out);
+int avsg_host_free(void* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AVSG_H */

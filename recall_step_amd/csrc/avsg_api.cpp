@@ -1,0 +1,255 @@
+// Host side of the C ABI declared in include/avsg.h: validation, handle and
+// workspace management, and the launch sequence of a recall step.
+#include "avsg.h"
+
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "internal.h"
+
+struct avsg_handle {
+    avsg_config cfg;
+    avsg_buffers bufs;
+    const uint8_t* host_dev;  // device alias of bufs.host_kv
+    int device;
+    size_t lds_bytes;
+    int gather_blocks;
+    int32_t* ws_pairs;        // [B][N_q][K][2] miss list when io gives none
+};
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip = int(e);
+    return AVSG_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool io_ok(const avsg_handle* h, const avsg_step_io* io) {
+    (void)h;
+    return io && io->topk && io->ctx_len && io->row_base && io->host_rows &&
+           io->slot_table && io->hit_mask && io->n_miss &&
+           (io->miss_pairs == nullptr || aligned16(io->miss_pairs));
+}
+
+int check_device(const avsg_handle* h) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    return dev == h->device ? AVSG_OK : AVSG_EINVAL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int avsg_version(void) { return AVSG_VERSION; }
+
+const char* avsg_strerror(int code) {
+    switch (code) {
+        case AVSG_OK: return "ok";
+        case AVSG_EINVAL: return "invalid argument or configuration";
+        case AVSG_ENOMEM: return "device memory allocation failed";
+        case AVSG_EHIP: return "HIP runtime call failed (see avsg_last_hip_error)";
+        case AVSG_EUNSUPPORTED: return "configuration beyond this build's limits";
+        default: return "unknown error code";
+    }
+}
+
+int avsg_last_hip_error(void) { return g_last_hip; }
+
+void avsg_config_default(avsg_config* cfg, int32_t B, int32_t N_q, int32_t K,
+                         int32_t S, int32_t row_bytes) {
+    if (!cfg) return;
+    cfg->B = B;
+    cfg->N_q = N_q;
+    cfg->K = K;
+    cfg->S = S;
+    cfg->L = 15;
+    cfg->R = 7;
+    cfg->a1 = 0x9E3779B1u;
+    cfg->a2 = 0x85EBCA77u;
+    cfg->a_fp = 0xC2B2AE3Du;
+    cfg->row_bytes = row_bytes;
+    cfg->flags = 0;
+    cfg->gather_blocks = 0;
+}
+
+int avsg_validate_config(const avsg_config* c) {
+    if (!c) return AVSG_EINVAL;
+    if (c->B < 1 || c->N_q < 1 || c->K < 1 || c->K > 8192) return AVSG_EINVAL;
+    if (c->S < 16 || c->S > 65536 || (c->S & (c->S - 1)) != 0) return AVSG_EINVAL;
+    if (int64_t(c->N_q) * c->K > c->S) return AVSG_EINVAL;
+    if (c->L < 1 || c->L > 127 || c->R < 0) return AVSG_EINVAL;
+    if ((c->a1 & 1u) == 0 || (c->a2 & 1u) == 0 || (c->a_fp & 1u) == 0) return AVSG_EINVAL;
+    if (c->row_bytes < 16 || (c->row_bytes & 15) != 0) return AVSG_EINVAL;
+    if (c->gather_blocks < 0) return AVSG_EINVAL;
+    if (c->flags & ~AVSG_FLAG_SKIP_GATHER) return AVSG_EINVAL;
+    return AVSG_OK;
+}
+
+size_t avsg_stage1_lds_bytes(const avsg_config* c) {
+    if (!c) return 0;
+    return avsg::stage1_layout(c->S, c->K, c->L).total;
+}
+
+size_t avsg_workspace_bytes(const avsg_config* c) {
+    if (!c) return 0;
+    return size_t(c->B) * c->N_q * c->K * 2 * sizeof(int32_t);
+}
+
+int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** out) {
+    if (!out) return AVSG_EINVAL;
+    *out = nullptr;
+    int rc = avsg_validate_config(cfg);
+    if (rc != AVSG_OK) return rc;
+    if (!bufs || !bufs->Q || !bufs->C || !bufs->F || !bufs->CNT || !bufs->dev_kv)
+        return AVSG_EINVAL;
+    if (!aligned16(bufs->Q) || !aligned16(bufs->C) || !aligned16(bufs->F) ||
+        !aligned16(bufs->CNT) || !aligned16(bufs->dev_kv))
+        return AVSG_EINVAL;
+    const bool skip = (cfg->flags & AVSG_FLAG_SKIP_GATHER) != 0;
+    if (!skip && (!bufs->host_kv || !aligned16(bufs->host_kv))) return AVSG_EINVAL;
+    if (bufs->host_rows_total < 0) return AVSG_EINVAL;
+    if (int64_t(cfg->B) * cfg->N_q > avsg::kMaxTokens) return AVSG_EUNSUPPORTED;
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    const size_t lds = avsg_stage1_lds_bytes(cfg);
+    if (lds > size_t(prop.sharedMemPerBlock)) return AVSG_EUNSUPPORTED;
+    e = avsg::stage1_prepare(lds);
+    if (e != hipSuccess) return hip_fail(e);
+
+    const uint8_t* host_dev = nullptr;
+    if (bufs->host_kv) {
+        void* dptr = nullptr;
+        e = hipHostGetDevicePointer(&dptr, const_cast<void*>(bufs->host_kv), 0);
+        if (e != hipSuccess) return hip_fail(e);
+        host_dev = static_cast<const uint8_t*>(dptr);
+    }
+
+    avsg_handle* h = new (std::nothrow) avsg_handle();
+    if (!h) return AVSG_ENOMEM;
+    h->cfg = *cfg;
+    h->bufs = *bufs;
+    h->host_dev = host_dev;
+    h->device = dev;
+    h->lds_bytes = lds;
+    h->gather_blocks = cfg->gather_blocks > 0 ? cfg->gather_blocks
+                                              : 4 * prop.multiProcessorCount;
+    e = hipMalloc(reinterpret_cast<void**>(&h->ws_pairs), avsg_workspace_bytes(cfg));
+    if (e != hipSuccess) {
+        g_last_hip = int(e);
+        delete h;
+        return AVSG_ENOMEM;
+    }
+    *out = h;
+    return AVSG_OK;
+}
+
+int avsg_destroy(avsg_handle* h) {
+    if (!h) return AVSG_OK;
+    hipError_t e = hipSuccess;
+    if (h->ws_pairs) e = hipFree(h->ws_pairs);
+    delete h;
+    return e == hipSuccess ? AVSG_OK : hip_fail(e);
+}
+
+int avsg_state_init(avsg_handle* h, const int32_t* row_mask, void* stream) {
+    if (!h) return AVSG_EINVAL;
+    int rc = check_device(h);
+    if (rc != AVSG_OK) return rc;
+    avsg::InitArgs a{h->bufs.Q, h->bufs.C, h->bufs.F, h->bufs.CNT, row_mask,
+                     h->cfg.B, h->cfg.S};
+    hipError_t e = avsg::launch_state_init(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? AVSG_OK : hip_fail(e);
+}
+
+int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
+    if (!h || !io_ok(h, io)) return AVSG_EINVAL;
+    int rc = check_device(h);
+    if (rc != AVSG_OK) return rc;
+    const avsg_config& c = h->cfg;
+    avsg::Stage1Args a;
+    a.Q = h->bufs.Q;
+    a.C = h->bufs.C;
+    a.F = h->bufs.F;
+    a.CNT = h->bufs.CNT;
+    a.topk = io->topk;
+    a.ctx_len = io->ctx_len;
+    a.row_base = io->row_base;
+    a.host_rows = io->host_rows;
+    a.slot_table = io->slot_table;
+    a.hit_mask = io->hit_mask;
+    a.n_miss = io->n_miss;
+    a.pairs = io->miss_pairs ? io->miss_pairs : h->ws_pairs;
+    a.host_rows_total = h->bufs.host_rows_total;
+    a.B = c.B;
+    a.Nq = c.N_q;
+    a.K = c.K;
+    a.S = c.S;
+    a.L = c.L;
+    a.R = c.R;
+    a.a1 = c.a1;
+    a.a2 = c.a2;
+    a.afp = c.a_fp;
+    hipError_t e = avsg::launch_stage1(a, h->lds_bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? AVSG_OK : hip_fail(e);
+}
+
+int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream) {
+    if (!h || !io_ok(h, io)) return AVSG_EINVAL;
+    if (!h->host_dev) return AVSG_EINVAL;
+    int rc = check_device(h);
+    if (rc != AVSG_OK) return rc;
+    const avsg_config& c = h->cfg;
+    avsg::GatherArgs a;
+    a.n_miss = io->n_miss;
+    a.pairs = io->miss_pairs ? io->miss_pairs : h->ws_pairs;
+    a.row_base = io->row_base;
+    a.host_rows = io->host_rows;
+    a.host = h->host_dev;
+    a.dev = static_cast<uint8_t*>(h->bufs.dev_kv);
+    a.host_rows_total = h->bufs.host_rows_total;
+    a.B = c.B;
+    a.Nq = c.N_q;
+    a.K = c.K;
+    a.S = c.S;
+    a.row_bytes = c.row_bytes;
+    hipError_t e = avsg::launch_gather(a, h->gather_blocks, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? AVSG_OK : hip_fail(e);
+}
+
+int avsg_step(avsg_handle* h, const avsg_step_io* io, void* stream) {
+    int rc = avsg_match(h, io, stream);
+    if (rc != AVSG_OK) return rc;
+    if (h->cfg.flags & AVSG_FLAG_SKIP_GATHER) return AVSG_OK;
+    return avsg_gather(h, io, stream);
+}
+
+int avsg_host_alloc(size_t bytes, void** out) {
+    if (!out || bytes == 0) return AVSG_EINVAL;
+    *out = nullptr;
+    hipError_t e = hipHostMalloc(out, bytes, hipHostMallocMapped);
+    if (e != hipSuccess) {
+        *out = nullptr;
+        return hip_fail(e);
+    }
+    return AVSG_OK;
+}
+
+int avsg_host_free(void* p) {
+    if (!p) return AVSG_OK;
+    hipError_t e = hipHostFree(p);
+    return e == hipSuccess ? AVSG_OK : hip_fail(e);
+}
+
+}  // extern "C"

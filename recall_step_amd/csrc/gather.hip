@@ -1,0 +1,148 @@
+// Stage Two of the recall step: copy every missed KV row from pinned host
+// memory into its device slot.
+//
+// Method: AVSG page, section 3.4 (each miss x_i moves from host position x_i
+// to device slot o_i, read directly from host memory with no staging copy)
+// and sections 1 / 4.3 (the missed rows are divided evenly across cores, not
+// by request or by top-K position).
+//
+// gfx950 mapping.  A fixed grid of workgroups reads the host pool through its
+// device-mapped address (zero-copy loads over the host link).  Every
+// workgroup scans the per-token miss counts itself, so the total M never
+// leaves the device and the grid needs no host decision; workgroup w then
+// copies flat misses [w*M/G, (w+1)*M/G).  Rows are resolved 64 at a time into
+// LDS (source and destination byte offsets), after which consecutive lanes
+// move consecutive 16-byte chunks of a row: one wave reads 1 KiB of a row's
+// contiguous host bytes per instruction, and each lane keeps several loads in
+// flight before storing.
+#include "internal.h"
+
+namespace avsg {
+namespace {
+
+constexpr int T = kGatherThreads;
+constexpr int kUnroll = 4;
+
+__device__ inline int wave_incl_scan(int v) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
+    extern __shared__ int32_t sOff[];  // [ntok + 1] exclusive prefix of n
+    __shared__ int64_t sSrc[kGatherRowsPerPass];
+    __shared__ int64_t sDst[kGatherRowsPerPass];
+    __shared__ int32_t sWave[T / 64 + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = __lane_id();
+    const int w = tid >> 6;
+    const int ntok = a.B * a.Nq;
+
+    // Exclusive scan of the miss counts, in chunks of T tokens.
+    int carry = 0;
+    for (int base = 0; base < ntok; base += T) {
+        const int k = base + tid;
+        int v = k < ntok ? a.n_miss[k] : 0;
+        v = min(max(v, 0), a.K);
+        const int incl = wave_incl_scan(v);
+        if (lane == 63) sWave[w] = incl;
+        __syncthreads();
+        if (w == 0) {
+            const int t = lane < T / 64 ? sWave[lane] : 0;
+            const int ti = wave_incl_scan(t);
+            if (lane < T / 64) sWave[lane] = ti - t;
+            if (lane == T / 64 - 1) sWave[T / 64] = ti;
+        }
+        __syncthreads();
+        if (k < ntok) sOff[k] = carry + incl - v + sWave[w];
+        carry += sWave[T / 64];
+        __syncthreads();
+    }
+    if (tid == 0) sOff[ntok] = carry;
+    __syncthreads();
+
+    const int64_t M = carry;
+    const int64_t lo = M * blockIdx.x / gridDim.x;
+    const int64_t hi = M * (blockIdx.x + 1) / gridDim.x;
+    const int cpr = a.row_bytes >> 4;  // 16-byte chunks per row
+
+    for (int64_t base = lo; base < hi; base += kGatherRowsPerPass) {
+        const int nrows = int(min<int64_t>(kGatherRowsPerPass, hi - base));
+        if (tid < nrows) {
+            const int32_t m = int32_t(base + tid);
+            // Token of flat miss m: last k with sOff[k] <= m.
+            int l = 0, h = ntok - 1;
+            while (l < h) {
+                const int mid = (l + h + 1) >> 1;
+                if (sOff[mid] <= m) l = mid; else h = mid - 1;
+            }
+            const int tok = l;
+            const int r = m - sOff[tok];
+            const int bq = tok / a.Nq;
+            const int2 pr = reinterpret_cast<const int2*>(a.pairs)[size_t(tok) * a.K + r];
+            const int64_t rb = a.row_base[bq];
+            const int32_t hr = a.host_rows[bq];
+            const bool ok = pr.x >= 0 && pr.x < hr && pr.y >= 0 && pr.y < a.S &&
+                            rb >= 0 && rb + hr <= a.host_rows_total;
+            sSrc[tid] = ok ? (rb + pr.x) * int64_t(a.row_bytes) : int64_t(-1);
+            sDst[tid] = (int64_t(bq) * a.S + pr.y) * int64_t(a.row_bytes);
+        }
+        __syncthreads();
+        const int items = nrows * cpr;
+        for (int it0 = tid; it0 < items; it0 += T * kUnroll) {
+            int4 v[kUnroll];
+            uint8_t* dptr[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int it = it0 + u * T;
+                const int row = min(it, items - 1) / cpr;
+                const int c = min(it, items - 1) - row * cpr;
+                const int64_t src = sSrc[row];
+                const bool live = it < items && src >= 0;
+                dptr[u] = live ? a.dev + sDst[row] + int64_t(c) * 16 : nullptr;
+                v[u] = live ? *reinterpret_cast<const int4*>(a.host + src + int64_t(c) * 16)
+                            : make_int4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if (dptr[u]) *reinterpret_cast<int4*>(dptr[u]) = v[u];
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void state_init_kernel(InitArgs a) {
+    const int b = blockIdx.x;
+    if (a.row_mask && a.row_mask[b] == 0) return;
+    int32_t* q = a.Q + size_t(b) * a.S;
+    int32_t* c = a.C + size_t(b) * a.S;
+    int32_t* f = a.F + size_t(b) * a.S;
+    const int4 neg = make_int4(-1, -1, -1, -1);
+    for (int j = threadIdx.x; j < (a.S >> 2); j += blockDim.x) {
+        reinterpret_cast<int4*>(q)[j] = neg;
+        reinterpret_cast<int4*>(c)[j] = neg;
+        reinterpret_cast<int4*>(f)[j] = neg;
+    }
+    if (threadIdx.x < 8) a.CNT[size_t(b) * 8 + threadIdx.x] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s) {
+    const size_t lds = size_t(a.B * a.Nq + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(T), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_init(const InitArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(state_init_kernel, dim3(a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace avsg

@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports what include/avsg.h declares, and its
+host-only entry points behave as documented (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import recall_step_amd as r
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "avsg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(avsg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(r.lib, n), n
+    assert set(names) == set(r.EXPORTED)
+
+
+def test_version_and_strerror():
+    assert r.avsg_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert r.avsg_strerror(code)
+    assert "unknown" in r.avsg_strerror(-99)
+
+
+def test_config_default_values():
+    c = r.avsg_config_default(8, 1, 2048, 2048, 1280)
+    assert (c.B, c.N_q, c.K, c.S, c.row_bytes) == (8, 1, 2048, 2048, 1280)
+    assert (c.L, c.R, c.a1, c.a2, c.a_fp) == (15, 7, 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D)
+    assert (c.flags, c.gather_blocks) == (0, 0)
+    assert r.avsg_validate_config(c) == 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("S", 3000), ("S", 8), ("S", 131072), ("K", 0), ("K", 4096), ("B", 0),
+    ("N_q", 0), ("L", 0), ("L", 128), ("R", -1), ("a1", 2), ("a2", 4),
+    ("a_fp", 0), ("row_bytes", 1000), ("row_bytes", 0), ("flags", 8),
+    ("gather_blocks", -1)])
+def test_invalid_configs_rejected(field, value):
+    c = r.avsg_config_default(4, 1, 2048, 2048, 1280)
+    setattr(c, field, value)
+    assert r.avsg_validate_config(c) == r.AVSG_EINVAL
+
+
+def test_capacity_bound_enforced():
+    """N_q * K <= S (AVSG App. B slot preservation)."""
+    assert r.avsg_validate_config(r.avsg_config_default(1, 4, 2048, 8192, 1280)) == 0
+    assert r.avsg_validate_config(r.avsg_config_default(1, 4, 2049, 8192, 1280)) == r.AVSG_EINVAL
+
+
+def test_lds_and_workspace_sizes():
+    c = r.avsg_config_default(32, 1, 2048, 8192, 1280)
+    # 9 bytes per slot (two int32 arrays + int8 lifetimes) + 8 B per sort key
+    # + 4 B per victim + histogram + scratch.
+    lds = r.avsg_stage1_lds_bytes(c)
+    assert 9 * 8192 + 8 * 2048 + 4 * 2048 <= lds <= 9 * 8192 + 8 * 2048 + 4 * 2048 + 1024
+    assert lds <= 160 * 1024
+    assert r.avsg_workspace_bytes(c) == 32 * 1 * 2048 * 2 * 4
+
+
+def test_create_rejects_bad_arguments_before_touching_a_device():
+    c = r.avsg_config_default(1, 1, 16, 16, 16)
+    bufs = r.AvsgBuffers()
+    with pytest.raises(r.AvsgError) as e:
+        r.avsg_create(c, bufs)
+    assert e.value.code == r.AVSG_EINVAL
+    c.S = 24
+    with pytest.raises(r.AvsgError) as e:
+        r.avsg_create(c, r.AvsgBuffers(16, 16, 16, 16, 16, 16, 1))
+    assert e.value.code == r.AVSG_EINVAL
+    # misaligned state pointer
+    c.S = 16
+    with pytest.raises(r.AvsgError):
+        r.avsg_create(c, r.AvsgBuffers(17, 32, 48, 64, 80, 96, 1))
+
+
+def test_null_safe_destroy_and_free():
+    assert r.lib.avsg_destroy(None) == 0
+    assert r.lib.avsg_host_free(None) == 0
+    assert r.lib.avsg_step(None, None, None) == r.AVSG_EINVAL
+    assert r.lib.avsg_match(None, None, None) == r.AVSG_EINVAL
+    assert r.lib.avsg_gather(None, None, None) == r.AVSG_EINVAL
+    assert r.lib.avsg_state_init(None, None, None) == r.AVSG_EINVAL
+    out = ctypes.c_void_p()
+    assert r.lib.avsg_host_alloc(0, ctypes.byref(out)) == r.AVSG_EINVAL
+
+
+def test_product_does_not_import_the_oracle():
+    """The product path never routes through the oracle."""
+    import recall_step_amd
+    pkg = os.path.dirname(recall_step_amd.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(root, f)).read()
+                assert "oracle" not in text.lower(), f

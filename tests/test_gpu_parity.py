@@ -1,0 +1,193 @@
+"""Bit-exact parity of the HIP recall path with the CPU oracle (needs a GPU).
+
+Every test calls the library through its C ABI (via the ctypes binding) and
+compares against the oracle on the same seeded inputs: slot tables, hit
+masks, miss counts, the miss list (eviction victims), the state tensors, the
+counters and the device slot buffer, all bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from workloads import gen_fuzz, make
+
+from _parity import Pair, run_parity, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import recall_step_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_fuzz_corpus(chunk):
+    """Tiny random cases: padding, out-of-range and speculative ids, MTP,
+    lost mappings, R in {0, 1, 3, S-1}, L in {1, 2, 3, 5}."""
+    for seed in range(chunk, 160, 4):
+        run_parity(gen_fuzz(seed), kv_every=1)
+
+
+def test_tiny_full():
+    cnt = run_parity(make("tiny"), kv_every=1)
+    assert cnt[1] == 16 * 256
+
+
+def test_matching_full():
+    run_parity(make("matching"), kv_every=16)
+
+
+def test_mtp3_full():
+    cnt = run_parity(make("mtp3"), kv_every=8)
+    assert cnt[6] == 0
+
+
+def test_imbalanced_full():
+    run_parity(make("imbalanced"), kv_every=16)
+
+
+def test_residency_full():
+    run_parity(make("residency"), kv_every=32)
+
+
+@pytest.mark.parametrize("K,S", [(256, 512), (1000, 1024), (2048, 2048), (3000, 4096),
+                                 (4096, 8192), (1, 16), (64, 64)])
+def test_shape_sweep_stage_one(K, S):
+    """Ragged and maximal K, several S: every IPT template and slot-per-thread
+    split of the Stage-One kernel, without the copy."""
+    w = make("matching", steps=4)
+    rng = np.random.default_rng([K, S])
+    topk = np.full((4, 2, 1, K), -1, np.int32)
+    for t in range(4):
+        for b in range(2):
+            n = max(1, K - int(rng.integers(0, 5)))
+            topk[t, b, 0, :n] = rng.choice(65536, n, replace=False)
+    w.topk, w.B, w.K, w.S, w.steps = topk, 2, K, S, 4
+    w.ctx_len = w.ctx_len[:4, :2]
+    w.host_rows, w.row_base = w.host_rows[:2], w.row_base[:2]
+    run_parity(w, gather=False, label=f"sweep K={K} S={S}")
+
+
+def test_state_beyond_lds_is_unsupported():
+    """K = S = 8192 needs more than 160 KiB of LDS: create refuses it."""
+    import recall_step_amd as r
+    cfg = r.avsg_config_default(1, 1, 8192, 8192, 1280, flags=r.FLAG_SKIP_GATHER)
+    assert r.avsg_validate_config(cfg) == 0
+    with pytest.raises(r.AvsgError) as e:
+        r.RecallStep(cfg, None, 1 << 20)
+    assert e.value.code == r.AVSG_EUNSUPPORTED
+
+
+def test_mtp_capacity_edge():
+    """N_q * K == S with L = 1: the extra decay reaches its bound every token."""
+    w = make("mtp3", steps=4, B=2)
+    w.L = 1
+    run_parity(w, kv_every=1, label="mtp3 L=1")
+
+
+def test_state_init_resets_selected_rows():
+    import torch
+    w = make("tiny")
+    w2 = make("tiny")
+    # two requests over the same ids
+    w2.B = 2
+    w2.topk = np.concatenate([w.topk, w.topk[:, :, :, ::-1]], axis=1)
+    w2.ctx_len = np.concatenate([w.ctx_len, w.ctx_len], axis=1)
+    w2.host_rows = np.concatenate([w.host_rows, w.host_rows])
+    w2.row_base = np.array([0, 4096], np.int64)
+    say("[parity] state_init row mask")
+    p = Pair(w2)
+    try:
+        for t in range(6):
+            if t == 3:
+                mask = torch.tensor([0, 1], dtype=torch.int32, device=p.rs.Q.device)
+                p.rs.state_init(mask)
+                p.oracle.Q[1] = -1
+                p.oracle.C[1] = -1
+                p.oracle.F[1] = -1
+                p.oracle.CNT[1] = 0
+            p.gpu_step(t)
+            p.compare(p.oracle_step(t), f"row reset step {t}", check_kv=True)
+    finally:
+        p.close()
+
+
+def test_match_then_gather_entry_points_and_workspace_miss_list():
+    """avsg_match + avsg_gather with the miss list left in the library's
+    workspace give the same slot buffer as avsg_step."""
+    w = make("tiny")
+    say("[parity] match/gather split, workspace miss list")
+    p = Pair(w)
+    try:
+        for t in range(w.steps):
+            io = p.io(t, miss_pairs=False)
+            p.rs.match(io)
+            p.rs.gather(io)
+            ref = p.oracle_step(t)
+            p.torch.cuda.synchronize()
+            assert np.array_equal(p.rs.slot_table.cpu().numpy(), ref.slot_table)
+        assert np.array_equal(p.rs.dev_kv.cpu().numpy(), p.oracle.shadow)
+    finally:
+        p.close()
+
+
+def test_hip_graph_capture_and_replay():
+    """One step captured in a HIP graph replays to the same results as the
+    oracle; inputs change between replays through fixed buffers."""
+    import torch
+    w = make("matching", steps=8)
+    say("[parity] graph capture matching x8")
+    p = Pair(w)
+    try:
+        dev = p.rs.Q.device
+        topk_in = torch.empty_like(p.topk[0])
+        ctx_in = torch.empty_like(p.ctx[0])
+        io = p.rs.io(topk_in, ctx_in, p.row_base, p.host_rows)
+        # warm the first step eagerly (not captured), then capture step 1
+        topk_in.copy_(p.topk[0])
+        ctx_in.copy_(p.ctx[0])
+        p.rs.step(io)
+        p.compare(p.oracle_step(0), "graph eager step 0")
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                p.rs.step(io, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        for t in range(1, w.steps):
+            topk_in.copy_(p.topk[t])
+            ctx_in.copy_(p.ctx[t])
+            g.replay()
+            torch.cuda.synchronize()
+            p.compare(p.oracle_step(t), f"graph replay step {t}", check_kv=True)
+    finally:
+        p.close()
+
+
+def test_determinism_repeat_from_same_state():
+    import torch
+    w = make("matching", steps=3)
+    say("[parity] determinism")
+    p = Pair(w, gather=False)
+    try:
+        p.gpu_step(0)
+        p.gpu_step(1)
+        snap = [x.clone() for x in (p.rs.Q, p.rs.C, p.rs.F, p.rs.CNT)]
+        p.gpu_step(2)
+        first = [x.clone() for x in (p.rs.Q, p.rs.C, p.rs.F, p.rs.CNT, p.rs.slot_table)]
+        for dst, src in zip((p.rs.Q, p.rs.C, p.rs.F, p.rs.CNT), snap):
+            dst.copy_(src)
+        p.gpu_step(2)
+        torch.cuda.synchronize()
+        again = (p.rs.Q, p.rs.C, p.rs.F, p.rs.CNT, p.rs.slot_table)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+    finally:
+        p.close()
