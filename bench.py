@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-decode-step KV recall path on one MI355X.
+
+A step is one pass of the whole path over one batch: Stage One (probe,
+refresh, classify, allocate, link, invalidate) for every request and query
+token, then the zero-copy gather of every missed row from pinned host memory
+into the device slot buffer.  The default workload is the matching benchmark
+(batch 8, context 65536, K = 2048, S = 2048, 1280-byte rows); its 64 seeded
+selection steps are replayed in order from an empty buffer (warm-up steps
+first, then the timed ones, wrapping around if more steps are asked for).
+
+Inputs are resident in HBM (selections) and in pinned host memory (the KV
+pool, which is where the method keeps it) before the timed region starts.
+Kernel durations come from HIP events recorded on the stream the kernels run
+on; the CPU oracle is timed on the host cores beside it.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "recall-step latency (us) + effective host->HBM gather GB/s; match Mkeys/s"
+PCIE_GEN5_X16_GBPS = 64.0   # published per-direction peak of the host link
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="matching",
+                    choices=["tiny", "matching", "residency", "mtp3", "imbalanced"])
+    ap.add_argument("--gather-blocks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def hip_runtime():
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    return hip
+
+
+def pinned_h2d_peak(r, torch, stream, nbytes=1 << 30, reps=10):
+    """Best-of-N pinned hipMemcpyAsync host->device rate, GB/s."""
+    hip = hip_runtime()
+    pool = r.HostPool(nbytes)
+    pool.array[:] = 1
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = hip.hipMemcpyAsync(dst.data_ptr(), pool.ptr, nbytes, 1, stream.cuda_stream)
+        assert rc == 0, rc
+        e1.record(stream)
+        e1.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del dst
+    pool.close()
+    return best
+
+
+def contiguous_gather_peak(r, torch, stream, row_bytes=1280, rows=1 << 19, blocks=0):
+    """The gather kernel on a miss list of consecutive host rows: the
+    zero-copy streaming rate of the same kernel without scattered reads."""
+    B, K = 256, 2048
+    S = K
+    rows = min(rows, B * K)
+    pool = r.HostPool(rows * row_bytes)
+    pool.array[:] = 7
+    cfg = r.avsg_config_default(B, 1, K, S, row_bytes, gather_blocks=blocks)
+    rs = r.RecallStep(cfg, pool, rows, stream=stream)
+    per = rows // B
+    n = torch.full((B, 1), per, dtype=torch.int32, device="cuda")
+    ids = torch.arange(K, dtype=torch.int32, device="cuda").repeat(B, 1)
+    pairs = torch.stack([ids, ids], dim=-1).reshape(B, 1, K, 2).contiguous()
+    row_base = (torch.arange(B, dtype=torch.int64, device="cuda") * per)
+    host_rows = torch.full((B,), per, dtype=torch.int32, device="cuda")
+    io = r.AvsgStepIO(0, 0, row_base.data_ptr(), host_rows.data_ptr(),
+                      rs.slot_table.data_ptr(), rs.hit_mask.data_ptr(),
+                      n.data_ptr(), pairs.data_ptr())
+    best = 0.0
+    for _ in range(8):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        r.avsg_gather(rs.handle, io, stream.cuda_stream)
+        e1.record(stream)
+        e1.synchronize()
+        best = max(best, per * B * row_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    rs.close()
+    pool.close()
+    return best
+
+
+def cpu_baseline(w, host_array, warmup, steps, budget_s):
+    """The CPU oracle as it stands, single thread, on the same steps."""
+    import oracle
+    per_pass = []
+    t_start = time.perf_counter()
+    passes = 0
+    while True:
+        o = oracle.Oracle.for_workload(w, host_kv=host_array)
+        for t in range(warmup):
+            k = t % w.steps
+            o.step(w.topk[k], w.ctx_len[k], w.row_base, w.host_rows)
+        t0 = time.perf_counter()
+        for t in range(warmup, warmup + steps):
+            k = t % w.steps
+            o.step(w.topk[k], w.ctx_len[k], w.row_base, w.host_rows)
+        per_pass.append((time.perf_counter() - t0) / steps)
+        passes += 1
+        if time.perf_counter() - t_start >= budget_s or passes >= 50:
+            break
+    return statistics.median(per_pass), passes
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the recall path shards by request "
+              f"with no exchange between GPUs, and this build measures one GPU's "
+              f"share; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        return 2
+    import torch
+    import recall_step_amd as r
+    from workloads import make
+
+    torch.cuda.set_device(0)
+    w = make(args.workload)
+    log(f"[bench] workload {w.name}: B={w.B} Nq={w.Nq} K={w.K} S={w.S} "
+        f"row={w.row_bytes} host_bytes={w.host_bytes} steps={args.steps} warmup={args.warmup}")
+    stream = torch.cuda.Stream()
+    host = r.HostPool(w.host_bytes)
+    w.fill_host_kv(host.array)
+    cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
+                                a1=w.a1, a2=w.a2, a_fp=w.afp,
+                                gather_blocks=args.gather_blocks)
+    rs = r.RecallStep(cfg, host, w.host_rows_total, stream=stream)
+    topk = torch.from_numpy(np.ascontiguousarray(w.topk)).cuda()
+    ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).cuda()
+    row_base = torch.from_numpy(w.row_base).cuda()
+    host_rows = torch.from_numpy(w.host_rows).cuda()
+    ios = [rs.io(topk[t], ctx[t], row_base, host_rows) for t in range(w.steps)]
+    sh = stream.cuda_stream
+    torch.cuda.synchronize()
+
+    for t in range(args.warmup):
+        rs.step(ios[t % w.steps], stream)
+    torch.cuda.synchronize()
+    cnt0 = rs.CNT.cpu().numpy().astype(np.int64)
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        io = ios[(args.warmup + k) % w.steps]
+        e = ev[k]
+        e[0].record(stream)
+        r.avsg_match(rs.handle, io, sh)
+        e[1].record(stream)
+        r.avsg_gather(rs.handle, io, sh)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    cnt1 = rs.CNT.cpu().numpy().astype(np.int64)
+    d = (cnt1 - cnt0).sum(0)
+    s1_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    g_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    misses, lookups, hits = int(d[r.CNT_MISSES]), int(d[r.CNT_LOOKUPS]), int(d[r.CNT_HITS])
+    visits = int(d[r.CNT_PROBE_VISITS])
+    gather_bytes = misses * w.row_bytes
+    s1_avg_s = sum(s1_ms) * 1e-3 / K
+    g_avg_s = sum(g_ms) * 1e-3 / K
+    step_us = wall / K * 1e6
+    gather_gbps = gather_bytes / (sum(g_ms) * 1e-3) / 1e9
+    mkeys = lookups / (sum(s1_ms) * 1e-3) / 1e6
+
+    # Stage One algorithmic HBM bytes per launch (per step): lifetimes read
+    # and written once per request (2*S*4 B), 4 B id in + 4 B slot out + 1 B
+    # mask out per lookup, 8 B (word + cached id) per bucket visited, 20 B per
+    # miss (install 12 B + miss list 8 B), 4 B count per token.
+    s1_bytes_step = (w.B * 2 * w.S * 4 + lookups / K * 9 + visits / K * 8 +
+                     misses / K * 20 + w.B * w.Nq * 4)
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N_q": w.Nq, "K": w.K, "S": w.S,
+                   "row_bytes": w.row_bytes, "context": int(w.host_rows.max()),
+                   "L": w.L, "R": w.R, "parallelism": "single GPU"},
+        "gather_GBps": round(gather_gbps, 2),
+        "match_Mkeys_per_s": round(mkeys, 1),
+        "stage1_us": round(s1_avg_s * 1e6, 2),
+        "gather_us": round(g_avg_s * 1e6, 2),
+        "stage1_us_p50_p90": [round(float(np.percentile(s1_ms, q)) * 1e3, 2) for q in (50, 90)],
+        "gather_us_p50_p90": [round(float(np.percentile(g_ms, q)) * 1e3, 2) for q in (50, 90)],
+        "misses_per_step": round(misses / K, 1),
+        "hit_rate": round(hits / lookups, 4) if lookups else 0.0,
+        "lost_mappings_per_step": round(float(d[r.CNT_LOST_COLLISION] + d[r.CNT_LOST_EXHAUSTED]) / K, 1),
+        "roofline": {
+            "bound": "pcie",
+            "achieved": round(gather_gbps, 2),
+            "peak": PCIE_GEN5_X16_GBPS,
+            "unit": "GB/s",
+            "frac": round(gather_gbps / PCIE_GEN5_X16_GBPS, 4),
+            "traffic": None,
+            "kernel": "gather_kernel",
+            "bytes_per_launch": round(gather_bytes / K),
+        },
+        "roofline_stage1": {
+            "bound": "hbm",
+            "achieved": round(s1_bytes_step / s1_avg_s / 1e9, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(s1_bytes_step / s1_avg_s / 1e9 / HBM_PEAK_GBPS, 5),
+            "kernel": "stage1_kernel",
+            "bytes_per_launch": round(s1_bytes_step),
+        },
+    }
+
+    if not args.no_peaks:
+        log("[bench] measuring pinned memcpy and contiguous zero-copy peaks")
+        peak = pinned_h2d_peak(r, torch, stream)
+        contig = contiguous_gather_peak(r, torch, stream, w.row_bytes,
+                                        blocks=args.gather_blocks)
+        result["pinned_h2d_memcpy_peak_GBps"] = round(peak, 2)
+        result["contiguous_gather_GBps"] = round(contig, 2)
+        result["gather_frac_of_memcpy_peak"] = round(gather_gbps / peak, 4)
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the same steps")
+        per_step, passes = cpu_baseline(w, host.array, args.warmup, K, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(per_step * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name} workload, full batch, the same {K} timed steps after "
+                      f"{args.warmup} warm-up steps, {passes} passes from an empty "
+                      f"buffer, median per-step time (single thread, gcc -O2)",
+        }
+
+    rs.close()
+    host.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

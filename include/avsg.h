@@ -190,7 +190,8 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream);
 /* Stage Two (AVSG s3.4): copy the host row of every miss listed by the last
  * avsg_match on this io into its slot of dev_kv, with the missed rows split
  * evenly across workgroups by flat miss index (not by request).  Reads
- * n_miss, the miss list and row_base.  AVSG_EINVAL if host_kv is NULL. */
+ * n_miss, the miss list, row_base and host_rows (topk, ctx_len, slot_table
+ * and hit_mask may be NULL).  AVSG_EINVAL if host_kv is NULL. */
 int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream);
 
 /* avsg_match followed by avsg_gather (the gather is skipped under

@@ -29,10 +29,16 @@ int hip_fail(hipError_t e) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool io_ok(const avsg_handle* h, const avsg_step_io* io) {
-    (void)h;
+// Fields Stage One reads or writes.
+bool match_io_ok(const avsg_step_io* io) {
     return io && io->topk && io->ctx_len && io->row_base && io->host_rows &&
            io->slot_table && io->hit_mask && io->n_miss &&
+           (io->miss_pairs == nullptr || aligned16(io->miss_pairs));
+}
+
+// Fields Stage Two reads.
+bool gather_io_ok(const avsg_step_io* io) {
+    return io && io->row_base && io->host_rows && io->n_miss &&
            (io->miss_pairs == nullptr || aligned16(io->miss_pairs));
 }
 
@@ -174,7 +180,7 @@ int avsg_state_init(avsg_handle* h, const int32_t* row_mask, void* stream) {
 }
 
 int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
-    if (!h || !io_ok(h, io)) return AVSG_EINVAL;
+    if (!h || !match_io_ok(io)) return AVSG_EINVAL;
     int rc = check_device(h);
     if (rc != AVSG_OK) return rc;
     const avsg_config& c = h->cfg;
@@ -206,7 +212,7 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
 }
 
 int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream) {
-    if (!h || !io_ok(h, io)) return AVSG_EINVAL;
+    if (!h || !gather_io_ok(io)) return AVSG_EINVAL;
     if (!h->host_dev) return AVSG_EINVAL;
     int rc = check_device(h);
     if (rc != AVSG_OK) return rc;
