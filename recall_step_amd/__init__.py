@@ -15,15 +15,17 @@ import ctypes
 import os
 
 import numpy as np
+# torch ships its own HIP runtime with the same soname as ROCm's.  Loading it
+# first makes the library below bind to that one copy; loading the library
+# first would put two HIP runtimes in the process.
+import torch  # noqa: F401
 
-from . import build as _build
-
-_LIB_PATH = _build.LIB
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libavsg.so")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
         f"{_LIB_PATH} is missing: build the HIP library first "
-        "(python -m recall_step_amd.build, or __graft_entry__.build())")
+        "(python recall_step_amd/build.py, or __graft_entry__.build())")
 
 lib = ctypes.CDLL(_LIB_PATH)
 
