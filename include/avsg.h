@@ -91,6 +91,9 @@ typedef struct avsg_config {
     uint32_t flags;    /* AVSG_FLAG_* */
     int32_t gather_blocks; /* Stage-Two workgroups; 0 = chosen from the CU
                               count */
+    int32_t stage1_threads; /* Stage-One workgroup size: 256, 512 or 1024
+                              with K <= 8 * stage1_threads; 0 = chosen from K
+                              (a tuning knob: results do not depend on it) */
 } avsg_config;
 
 /* Caller-owned buffers bound at create time. */
@@ -147,7 +150,7 @@ int avsg_last_hip_error(void);
 
 /* Fill cfg with the given shape and the defaults L = 15, R = 7,
  * a1 = 0x9E3779B1, a2 = 0x85EBCA77, a_fp = 0xC2B2AE3D, flags = 0,
- * gather_blocks = 0. */
+ * gather_blocks = 0, stage1_threads = 0. */
 void avsg_config_default(avsg_config* cfg, int32_t B, int32_t N_q, int32_t K,
                          int32_t S, int32_t row_bytes);
 
@@ -156,9 +159,9 @@ void avsg_config_default(avsg_config* cfg, int32_t B, int32_t N_q, int32_t K,
 int avsg_validate_config(const avsg_config* cfg);
 
 /* LDS bytes the Stage-One kernel needs for cfg (one workgroup holds one
- * request's bucket words, ids and lifetimes).  avsg_create returns
- * AVSG_EUNSUPPORTED if this exceeds the device's per-workgroup LDS.  Needs
- * no GPU. */
+ * request's bucket words, ids and lifetimes, 9 bytes per slot, plus per-token
+ * work space), or 0 if cfg does not fit in 160 KiB (gfx950's per-workgroup
+ * LDS); avsg_create then returns AVSG_EUNSUPPORTED.  Needs no GPU. */
 size_t avsg_stage1_lds_bytes(const avsg_config* cfg);
 
 /* Device bytes avsg_create allocates for its workspace.  Needs no GPU. */

@@ -48,7 +48,8 @@ class AvsgConfig(ctypes.Structure):
                 ("L", ctypes.c_int32), ("R", ctypes.c_int32),
                 ("a1", ctypes.c_uint32), ("a2", ctypes.c_uint32),
                 ("a_fp", ctypes.c_uint32), ("row_bytes", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("gather_blocks", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("gather_blocks", ctypes.c_int32),
+                ("stage1_threads", ctypes.c_int32)]
 
 
 class AvsgBuffers(ctypes.Structure):

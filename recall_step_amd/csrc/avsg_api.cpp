@@ -15,6 +15,7 @@ struct avsg_handle {
     int device;
     size_t lds_bytes;
     int gather_blocks;
+    int stage1_threads;
     int32_t* ws_pairs;        // [B][N_q][K][2] miss list when io gives none
 };
 
@@ -83,6 +84,7 @@ void avsg_config_default(avsg_config* cfg, int32_t B, int32_t N_q, int32_t K,
     cfg->row_bytes = row_bytes;
     cfg->flags = 0;
     cfg->gather_blocks = 0;
+    cfg->stage1_threads = 0;
 }
 
 int avsg_validate_config(const avsg_config* c) {
@@ -94,6 +96,11 @@ int avsg_validate_config(const avsg_config* c) {
     if ((c->a1 & 1u) == 0 || (c->a2 & 1u) == 0 || (c->a_fp & 1u) == 0) return AVSG_EINVAL;
     if (c->row_bytes < 16 || (c->row_bytes & 15) != 0) return AVSG_EINVAL;
     if (c->gather_blocks < 0) return AVSG_EINVAL;
+    if (c->stage1_threads != 0 && c->stage1_threads != 256 && c->stage1_threads != 512 &&
+        c->stage1_threads != 1024)
+        return AVSG_EINVAL;
+    if (c->stage1_threads != 0 && c->K > c->stage1_threads * avsg::kMaxIdsPerThread)
+        return AVSG_EINVAL;
     if (c->flags & ~AVSG_FLAG_SKIP_GATHER) return AVSG_EINVAL;
     return AVSG_OK;
 }
@@ -130,7 +137,7 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** 
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e);
     const size_t lds = avsg_stage1_lds_bytes(cfg);
-    if (lds > size_t(prop.sharedMemPerBlock)) return AVSG_EUNSUPPORTED;
+    if (lds == 0 || lds > size_t(prop.sharedMemPerBlock)) return AVSG_EUNSUPPORTED;
     e = avsg::stage1_prepare(lds);
     if (e != hipSuccess) return hip_fail(e);
 
@@ -151,6 +158,7 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** 
     h->lds_bytes = lds;
     h->gather_blocks = cfg->gather_blocks > 0 ? cfg->gather_blocks
                                               : 4 * prop.multiProcessorCount;
+    h->stage1_threads = avsg::stage1_threads(cfg->K, cfg->stage1_threads);
     e = hipMalloc(reinterpret_cast<void**>(&h->ws_pairs), avsg_workspace_bytes(cfg));
     if (e != hipSuccess) {
         g_last_hip = int(e);
@@ -207,7 +215,8 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
     a.a1 = c.a1;
     a.a2 = c.a2;
     a.afp = c.a_fp;
-    hipError_t e = avsg::launch_stage1(a, h->lds_bytes, static_cast<hipStream_t>(stream));
+    hipError_t e = avsg::launch_stage1(a, h->stage1_threads, h->lds_bytes,
+                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }
 

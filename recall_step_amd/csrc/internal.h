@@ -7,11 +7,20 @@
 
 namespace avsg {
 
-// Stage One runs one 1024-thread workgroup (16 wave64s) per request.
-constexpr int kStage1Threads = 1024;
-constexpr int kStage1Waves = kStage1Threads / 64;
-// Largest number of selected ids one Stage-One thread holds (K <= 8192).
+// Stage One runs one workgroup per request of 256, 512 or 1024 threads (by
+// default two ids per thread, 1024 threads from K = 2048); each thread holds
+// up to kMaxIdsPerThread ids of a token.
+constexpr int kMaxWaves = 16;
 constexpr int kMaxIdsPerThread = 8;
+// LDS one Stage-One workgroup may use (gfx950: 160 KiB per workgroup).
+constexpr size_t kStage1LdsBudget = 160 * 1024;
+// The miss-rank bitmap covers at most this many consecutive ids.
+constexpr int kMaxBitmapIds = 1 << 18;
+// Copies of the lifetime histogram (lane % kHistCopies picks one).
+constexpr int kHistCopies = 16;
+// Lifetime words (4 slots each) one Stage-One thread owns: S <= 16384 fits
+// the LDS budget and a workgroup has at least 256 threads.
+constexpr int kMaxLifeWords = 16;
 
 // Stage Two: 256-thread workgroups, rows resolved in passes of this size.
 constexpr int kGatherThreads = 256;
@@ -28,20 +37,40 @@ __host__ __device__ inline int next_pow2(int v) {
 __host__ __device__ inline size_t round16(size_t v) { return (v + 15) & ~size_t(15); }
 
 // LDS layout of the Stage-One workgroup, in bytes from the base.
+//   q, c    int32 [S]  bucket words, cached ids
+//   f       uint8 [S]  lifetimes as G = F + 1 (0 = dead)
+//   vict    int32 [K]  victim slots (aliased by the uint16 rank-by-position
+//                      table of the sorting fallback)
+//   region  the larger of: uint64 [next_pow2(K)] sort keys; int2 [K] miss
+//           list; the miss-rank bitmap (bitmap_words uint32) followed by
+//           its per-word prefix counts (bitmap_words uint16)
+//   hist    int32 [kHistCopies][L+2] lifetime histogram copies
+//   scr     int32 [96]  reduction scratch, flags and counters
+// total is 0 when even the smallest region does not fit the budget.
 struct Stage1Layout {
-    size_t q, c, f, key, vict, hist, scr, total;
+    size_t q, c, f, vict, region, hist, scr, total;
+    int bitmap_words;
 };
 
 __host__ __device__ inline Stage1Layout stage1_layout(int S, int K, int L) {
     Stage1Layout o;
-    o.q = 0;                                   // int32 [S] bucket words
-    o.c = o.q + size_t(S) * 4;                 // int32 [S] cached ids
-    o.f = o.c + size_t(S) * 4;                 // int8  [S] lifetimes
-    o.key = round16(o.f + size_t(S));          // uint64 [next_pow2(K)] miss keys
-    o.vict = o.key + size_t(next_pow2(K)) * 8; // int32 [K] victim slots
-    o.hist = round16(o.vict + size_t(K) * 4);  // int32 [L+2] lifetime histogram
-    o.scr = round16(o.hist + size_t(L + 2) * 4);  // int32 [3][32] scan scratch
-    o.total = o.scr + 3 * 32 * 4;
+    o.q = 0;
+    o.c = o.q + size_t(S) * 4;
+    o.f = o.c + size_t(S) * 4;
+    o.vict = round16(o.f + size_t(S));
+    o.region = round16(o.vict + size_t(K) * 4);
+    const size_t tail = round16(size_t(kHistCopies) * (L + 2) * 4) + 96 * 4;
+    const size_t keys = size_t(next_pow2(K)) * 8;
+    size_t avail = o.region + tail < kStage1LdsBudget ? kStage1LdsBudget - o.region - tail : 0;
+    size_t words = avail / 6;  // 4 bytes of bits + 2 bytes of prefix per word
+    if (words > size_t(kMaxBitmapIds / 32)) words = kMaxBitmapIds / 32;
+    words &= ~size_t(7);
+    o.bitmap_words = int(words);
+    const size_t region = keys > words * 6 ? keys : words * 6;
+    o.hist = round16(o.region + region);
+    o.scr = round16(o.hist + size_t(kHistCopies) * (L + 2) * 4);
+    o.total = o.scr + 96 * 4;
+    if (o.total > kStage1LdsBudget) o.total = 0;
     return o;
 }
 
@@ -83,8 +112,10 @@ struct InitArgs {
     int32_t B, S;
 };
 
+// Stage-One workgroup size: `requested` if nonzero, else chosen from K.
+int stage1_threads(int K, int requested);
 hipError_t stage1_prepare(size_t lds_bytes);
-hipError_t launch_stage1(const Stage1Args& a, size_t lds_bytes, hipStream_t s);
+hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds_bytes, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s);
 hipError_t launch_state_init(const InitArgs& a, hipStream_t s);
 

@@ -7,60 +7,111 @@
 // sequence through one buffer) and Appendix B (single packed-word scatter,
 // exhausted probes, slot preservation, speculative invalidation).
 //
-// gfx950 mapping.  One 1024-thread workgroup owns one request for the whole
-// step.  Its bucket words and cached ids (int32) and its lifetimes (int8) are
-// staged in LDS once, every query token runs against the LDS copy, and the
-// state is written back once.  Each thread holds up to IPT consecutive ids of
-// a token.  Block-wide steps use wave64 shuffles and ballots plus a 16-entry
-// LDS carry: ordered miss compaction is an exclusive scan, the victim list is
-// an exclusive scan of dead flags in slot order, and the lifetime histogram
-// uses wave-aggregated LDS atomics.  Misses are sorted only when the token's
-// ids do not already arrive ascending.  Contested buckets are resolved with an
-// LDS atomicMax on the miss rank, so the result does not depend on wave
-// scheduling.
+// gfx950 mapping.  One workgroup owns one request for the whole step.  Its
+// bucket words and cached ids (int32) and its lifetimes are staged in LDS
+// once, every query token runs against the LDS copy, and the state is written
+// back once.  Lifetimes are held as one byte per slot, G = F + 1 (0 = dead,
+// L + 1 = just refreshed), so dead slots are zero bytes.
+//
+// A workgroup has 256 to 1024 threads, two ids per thread by default (up to
+// eight): the probe and link rounds are bound by LDS latency, which more
+// waves hide, while the fixed per-thread work (scans, reductions, barriers)
+// grows with the wave count; DPP scans and one-barrier workgroup reductions
+// keep that part small.
+//
+// Each thread owns IPT consecutive positions of a token's top-K list and
+// carries their ids through the whole token: it probes them, refreshes its
+// hits and, once it knows the rank of each of its misses among the token's
+// misses (ascending id), installs them into the victim of that rank, links
+// their bucket words and writes its slot-table and hit-mask entries with
+// vector stores.  The rank comes from a bitmap over [min id, max id] of the
+// token's misses held in LDS: one atomicOr per miss, then prefix popcounts
+// over the words, so rank(x) = (misses below x's word) + popc(word bits below
+// x).  When the ids span more than the bitmap or a missing id repeats, the
+// token falls back to a bitonic sort of (id, position) keys in LDS.
+//
+// Victims: the dead-slot count is an exclusive scan over slots in index
+// order; only when it is short of the miss count does the workgroup build a
+// lifetime histogram (16 LDS copies to spread atomics) to find the least
+// extra decay.  Contested buckets are resolved with an LDS atomicMax on the
+// miss rank, so no result depends on wave scheduling.  Wave scans use DPP
+// row shifts and row broadcasts; a workgroup scan needs one barrier.
 #include "internal.h"
 
 namespace avsg {
 namespace {
 
-constexpr int T = kStage1Threads;
-constexpr int W = kStage1Waves;
 constexpr int32_t kEmpty = -1;
 constexpr int32_t kClaimBase = INT32_MIN;
 
-__device__ inline int wave_incl_scan(int v) {
-    const int lane = __lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int u = __shfl_up(v, d, 64);
-        if (lane >= d) v += u;
-    }
-    return v;
-}
+// DPP controls (GFX9 encoding): row_shr:n = 0x110 + n, row_bcast:15 / :31.
+#define AVSG_DPP_SCAN(x, OP, ID)                                                  \
+    do {                                                                          \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x111, 0xf, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x112, 0xf, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x114, 0xf, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x118, 0xf, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x142, 0xa, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x143, 0xc, 0xf, false));    \
+    } while (0)
+
+__device__ inline int op_add(int a, int b) { return a + b; }
+__device__ inline int op_min(int a, int b) { return min(a, b); }
+__device__ inline int op_max(int a, int b) { return max(a, b); }
+
+// Inclusive wave64 scans.
+__device__ inline int wave_scan_add(int x) { AVSG_DPP_SCAN(x, op_add, 0); return x; }
+__device__ inline int wave_scan_min(int x) { AVSG_DPP_SCAN(x, op_min, INT32_MAX); return x; }
+__device__ inline int wave_scan_max(int x) { AVSG_DPP_SCAN(x, op_max, INT32_MIN); return x; }
+__device__ inline int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
 
 // Exclusive scan of one int per thread over the workgroup; *total gets the
-// sum.  scr needs W+1 ints and must not be in use by a scan still being read.
+// sum.  One barrier.  scr holds kMaxWaves ints; two consecutive workgroup
+// operations must use different scratch buffers.
+template <int T>
 __device__ inline int block_excl_scan(int v, int32_t* scr, int* total) {
-    const int lane = __lane_id();
+    constexpr int NW = T / 64;
     const int w = threadIdx.x >> 6;
-    int incl = wave_incl_scan(v);
-    if (lane == 63) scr[w] = incl;
+    const int incl = wave_scan_add(v);
+    if (__lane_id() == 63) scr[w] = incl;
     __syncthreads();
-    if (w == 0) {
-        int t = lane < W ? scr[lane] : 0;
-        int ti = wave_incl_scan(t);
-        if (lane < W) scr[lane] = ti - t;
-        if (lane == W - 1) scr[W] = ti;
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+        const int s = scr[u];
+        pre += u < w ? s : 0;
+        tot += s;
     }
-    __syncthreads();
-    *total = scr[W];
-    return incl - v + scr[w];
+    *total = tot;
+    return incl - v + pre;
 }
 
-__device__ inline int wave_sum(int v) {
+// Workgroup sum of v, min of lo and max of hi.  One barrier; scr holds
+// 3 * kMaxWaves ints.
+template <int T>
+__device__ inline void block_sum_min_max(int v, int lo, int hi, int32_t* scr, int* sum,
+                                         int* mn, int* mx) {
+    constexpr int NW = T / 64;
+    const int w = threadIdx.x >> 6;
+    v = lane63(wave_scan_add(v));
+    lo = lane63(wave_scan_min(lo));
+    hi = lane63(wave_scan_max(hi));
+    if (__lane_id() == 0) {
+        scr[w] = v;
+        scr[kMaxWaves + w] = lo;
+        scr[2 * kMaxWaves + w] = hi;
+    }
+    __syncthreads();
+    int s = 0, a = INT32_MAX, c = INT32_MIN;
 #pragma unroll
-    for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, 64);
-    return v;
+    for (int u = 0; u < NW; ++u) {
+        s += scr[u];
+        a = min(a, scr[kMaxWaves + u]);
+        c = max(c, scr[2 * kMaxWaves + u]);
+    }
+    *sum = s;
+    *mn = a;
+    *mx = c;
 }
 
 __device__ inline uint32_t home_bucket(uint32_t x, uint32_t a1, uint32_t smask) {
@@ -75,7 +126,13 @@ __device__ inline int32_t fp_of(uint32_t x, uint32_t afp) {
     return int32_t((x * afp) >> 17);
 }
 
+// 0x80 in every byte of x that is zero, 0 elsewhere (exact for all values).
+__device__ inline uint32_t zero_bytes(uint32_t x) {
+    return ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+}
+
 // Ascending bitonic sort of P (a power of two) 64-bit keys in LDS.
+template <int T>
 __device__ void bitonic_sort(uint64_t* key, int P) {
     for (int k = 2; k <= P; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
@@ -95,7 +152,65 @@ __device__ void bitonic_sort(uint64_t* key, int P) {
     }
 }
 
+// IPT consecutive ids of one token starting at X[i0]; ids past K read as -1.
 template <int IPT>
+__device__ inline void load_ids(const int32_t* __restrict__ X, int i0, int K, bool vec,
+                                int32_t (&x)[IPT]) {
+    if (vec && i0 + IPT <= K) {
+        if constexpr (IPT == 1) {
+            x[0] = X[i0];
+        } else if constexpr (IPT == 2) {
+            const int2 v = *reinterpret_cast<const int2*>(X + i0);
+            x[0] = v.x;
+            x[1] = v.y;
+        } else {
+#pragma unroll
+            for (int q = 0; q < IPT / 4; ++q) {
+                const int4 v = *reinterpret_cast<const int4*>(X + i0 + 4 * q);
+                x[4 * q] = v.x;
+                x[4 * q + 1] = v.y;
+                x[4 * q + 2] = v.z;
+                x[4 * q + 3] = v.w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < IPT; ++e) x[e] = i0 + e < K ? X[i0 + e] : -1;
+    }
+}
+
+template <int IPT>
+__device__ inline void store_outputs(int32_t* __restrict__ O, int8_t* __restrict__ H, int i0,
+                                     int K, bool vec, const int32_t (&o)[IPT],
+                                     const int8_t (&h)[IPT]) {
+    if (vec && i0 + IPT <= K) {
+        if constexpr (IPT == 1) {
+            O[i0] = o[0];
+            H[i0] = h[0];
+        } else if constexpr (IPT == 2) {
+            *reinterpret_cast<int2*>(O + i0) = make_int2(o[0], o[1]);
+            *reinterpret_cast<char2*>(H + i0) = make_char2(h[0], h[1]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < IPT / 4; ++q) {
+                *reinterpret_cast<int4*>(O + i0 + 4 * q) =
+                    make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+                *reinterpret_cast<char4*>(H + i0 + 4 * q) =
+                    make_char4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < IPT; ++e) {
+            if (i0 + e < K) {
+                O[i0 + e] = o[e];
+                H[i0 + e] = h[e];
+            }
+        }
+    }
+}
+
+template <int T, int IPT>
 __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int S = a.S, K = a.K, L = a.L, R = a.R;
@@ -103,34 +218,67 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     const Stage1Layout lay = stage1_layout(S, K, L);
     int32_t* sQ = reinterpret_cast<int32_t*>(smem + lay.q);
     int32_t* sC = reinterpret_cast<int32_t*>(smem + lay.c);
-    int8_t* sF = reinterpret_cast<int8_t*>(smem + lay.f);
-    uint64_t* sKey = reinterpret_cast<uint64_t*>(smem + lay.key);
+    uint8_t* sG = smem + lay.f;
+    uint32_t* sGw = reinterpret_cast<uint32_t*>(smem + lay.f);
     int32_t* sVict = reinterpret_cast<int32_t*>(smem + lay.vict);
-    int32_t* sHist = reinterpret_cast<int32_t*>(smem + lay.hist);
-    int32_t* sScrA = reinterpret_cast<int32_t*>(smem + lay.scr);
-    int32_t* sScrB = sScrA + 32;
-    int32_t* sMisc = sScrA + 64;
+    uint16_t* sRank = reinterpret_cast<uint16_t*>(smem + lay.vict);  // aliases sVict
+    uint64_t* sKey = reinterpret_cast<uint64_t*>(smem + lay.region);
+    uint32_t* sBits = reinterpret_cast<uint32_t*>(smem + lay.region);  // aliases sKey
+    uint16_t* sPre = reinterpret_cast<uint16_t*>(smem + lay.region + size_t(lay.bitmap_words) * 4);
+    int2* sPair = reinterpret_cast<int2*>(smem + lay.region);          // aliases sKey
+    int32_t* sHist = reinterpret_cast<int32_t*>(smem + lay.hist);       // [16][L + 2]
+    int32_t* sMM = reinterpret_cast<int32_t*>(smem + lay.scr);          // 3 * kMaxWaves
+    int32_t* sS0 = sMM + 3 * kMaxWaves;                                  // kMaxWaves
+    int32_t* sS1 = sS0 + kMaxWaves;                                      // kMaxWaves
+    int32_t* sMisc = sS1 + kMaxWaves;                                    // flags, counters
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = __lane_id();
+    const int HB = L + 2;  // histogram bins: G in [0, L + 1]
     int32_t* gQ = a.Q + size_t(b) * S;
     int32_t* gC = a.C + size_t(b) * S;
     int32_t* gF = a.F + size_t(b) * S;
+    // Vector loads and stores of a thread's IPT positions need K % IPT == 0
+    // and base pointers aligned to the vector size.
+    const bool vec = (K % IPT) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.topk) % (4 * IPT)) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.slot_table) % (4 * IPT)) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.hit_mask) % IPT) == 0;
+    const int i0 = tid * IPT;
 
-    // Stage the request's state; the once-per-step lifetime decay of the
-    // first token is fused into the load (lifetimes of a valid state are in
-    // [-1, L]; the clamp keeps histogram bins in range for any input).
-    for (int j = tid; j < (S >> 2); j += T) {
-        reinterpret_cast<int4*>(sQ)[j] = reinterpret_cast<const int4*>(gQ)[j];
-        reinterpret_cast<int4*>(sC)[j] = reinterpret_cast<const int4*>(gC)[j];
-        const int4 f = reinterpret_cast<const int4*>(gF)[j];
-        char4 f8;
-        f8.x = int8_t(min(max(f.x - 1, -1), L));
-        f8.y = int8_t(min(max(f.y - 1, -1), L));
-        f8.z = int8_t(min(max(f.z - 1, -1), L));
-        f8.w = int8_t(min(max(f.w - 1, -1), L));
-        reinterpret_cast<char4*>(sF)[j] = f8;
+    // First token's ids and the counters are fetched while the state is
+    // staged.
+    int32_t xn[IPT];
+    load_ids<IPT>(a.topk + size_t(b) * a.Nq * K, i0, K, vec, xn);
+    const int32_t cnt_old = tid < 8 ? a.CNT[size_t(b) * 8 + tid] : 0;
+
+    // Stage the request's state.  The once-per-step decay before the first
+    // token is fused into the load: G = max(F - 1, -1) + 1, clamped to
+    // [0, L + 1] for any input.
+    for (int j0 = tid; j0 < (S >> 2); j0 += 4 * T) {
+        // Loads clamped to the last word (always in bounds), stores guarded.
+        int4 q[4], c[4], f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = min(j0 + u * T, (S >> 2) - 1);
+            q[u] = reinterpret_cast<const int4*>(gQ)[j];
+            c[u] = reinterpret_cast<const int4*>(gC)[j];
+            f[u] = reinterpret_cast<const int4*>(gF)[j];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u * T;
+            if (j < (S >> 2)) {
+                reinterpret_cast<int4*>(sQ)[j] = q[u];
+                reinterpret_cast<int4*>(sC)[j] = c[u];
+                const uint32_t g0 = uint32_t(min(max(f[u].x, 0), L + 1));
+                const uint32_t g1 = uint32_t(min(max(f[u].y, 0), L + 1));
+                const uint32_t g2 = uint32_t(min(max(f[u].z, 0), L + 1));
+                const uint32_t g3 = uint32_t(min(max(f[u].w, 0), L + 1));
+                sGw[j] = g0 | (g1 << 8) | (g2 << 16) | (g3 << 24);
+            }
+        }
     }
 
     const int64_t rb = a.row_base[b];
@@ -138,235 +286,327 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     const bool row_ok = rb >= 0 && hr >= 0 && rb + hr <= a.host_rows_total;
     const int32_t N = a.ctx_len[b];
 
-    // This thread's contiguous slot range for S-wide passes.
-    const int E = S >= T ? S / T : 1;
-    const int j0 = tid * E;
-    const bool has_slots = j0 < S;
+    // This thread's contiguous run of lifetime words (4 slots each) for the
+    // S-wide passes.
+    const int nd = S >> 2;
+    const int D = nd >= T ? nd / T : 1;  // <= kMaxLifeWords (S <= 16384, T >= 256)
+    const int dw0 = tid * D;
+    const int dwn = dw0 < nd ? D : 0;
 
     uint32_t c_hits = 0, c_look = 0, c_lcol = 0, c_lexh = 0, c_live = 0, c_visit = 0;
     uint32_t c_err = 0, c_miss = 0;
 
-    if (tid == 0) sMisc[0] = 0;
     __syncthreads();
 
     for (int g = 0; g < a.Nq; ++g) {
         const size_t tok = size_t(b) * a.Nq + g;
-        const int32_t* X = a.topk + tok * K;
         int32_t* O = a.slot_table + tok * K;
         int8_t* H = a.hit_mask + tok * K;
-        const int i0 = tid * IPT;
 
-        for (int k = tid; k < L + 2; k += T) sHist[k] = 0;
+        int32_t x[IPT];
+#pragma unroll
+        for (int e = 0; e < IPT; ++e) x[e] = xn[e];
+        if (g + 1 < a.Nq) load_ids<IPT>(a.topk + (tok + 1) * K, i0, K, vec, xn);
+
+        for (int k = tid; k < kHistCopies * HB; k += T) sHist[k] = 0;
 
         // --- Pass 1/2: probe, refresh hits, classify -----------------------
-        int32_t x[IPT];
         int32_t slot[IPT];
         uint32_t pos[IPT], dst[IPT];
-        bool open[IPT], valid[IPT];
-        bool any_open = false;
+        uint32_t valid = 0;
 #pragma unroll
         for (int e = 0; e < IPT; ++e) {
-            const int i = i0 + e;
-            int32_t v = i < K ? X[i] : -1;
+            const int32_t v = x[e];
             const bool ok = v != -1 && row_ok && v >= 0 && v < hr;
             if (v != -1 && !ok) c_err |= 1u;
-            x[e] = v;
-            valid[e] = ok;
-            open[e] = ok;
+            valid |= uint32_t(ok) << e;
             slot[e] = -1;
             pos[e] = home_bucket(uint32_t(v), a.a1, smask);
             dst[e] = stride_of(uint32_t(v), a.a2, smask);
-            any_open |= ok;
         }
-        for (int t = 0; t <= R && any_open; ++t) {
-            any_open = false;
+        // Rounds in lock step over the thread's ids, every bucket word of a
+        // round loaded before any cached id, so the LDS round trips of all
+        // IPT ids overlap.
+        uint32_t open = valid;
+        for (int t = 0; t <= R; ++t) {
+            if (__ballot(open != 0u) == 0ull) break;
+            c_visit += uint32_t(__popc(open));
+            // Closed ids and empty buckets issue no LDS read.
+            int32_t wd[IPT], cc[IPT];
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) wd[e] = ((open >> e) & 1u) ? sQ[pos[e]] : kEmpty;
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) cc[e] = wd[e] != kEmpty ? sC[wd[e] & int32_t(smask)] : -2;
 #pragma unroll
             for (int e = 0; e < IPT; ++e) {
-                if (open[e]) {
-                    const int32_t wd = sQ[pos[e]];
-                    const int32_t s = wd & int32_t(smask);
-                    if (wd != kEmpty && sC[s] == x[e]) {
-                        slot[e] = s;
-                        open[e] = false;
-                        c_visit += uint32_t(t + 1);
-                    } else {
-                        pos[e] = (pos[e] + dst[e]) & smask;
-                        any_open = true;
-                    }
-                }
+                const bool hit = ((open >> e) & 1u) && wd[e] != kEmpty && cc[e] == x[e];
+                slot[e] = hit ? (wd[e] & int32_t(smask)) : slot[e];
+                open &= ~(uint32_t(hit) << e);
+                pos[e] = (pos[e] + dst[e]) & smask;
             }
         }
-        int m_local = 0;
+        // open now holds exactly the valid misses.
+        const uint32_t missm = open;
+        int lo_local = INT32_MAX, hi_local = INT32_MIN;
 #pragma unroll
         for (int e = 0; e < IPT; ++e) {
-            const int i = i0 + e;
-            if (valid[e]) {
-                ++c_look;
-                if (slot[e] >= 0) {
-                    sF[slot[e]] = int8_t(L);
-                    O[i] = slot[e];
-                    H[i] = 1;
-                    ++c_hits;
-                } else {
-                    ++m_local;
-                    c_visit += uint32_t(R + 1);
-                }
-            } else if (i < K) {
-                O[i] = -1;
-                H[i] = -1;
+            if (missm & (1u << e)) {
+                lo_local = min(lo_local, x[e]);
+                hi_local = max(hi_local, x[e]);
+            } else if (valid & (1u << e)) {
+                sG[slot[e]] = uint8_t(L + 1);
             }
         }
+        const int m_local = __popc(missm);
+        c_look += uint32_t(__popc(valid));
+        c_hits += uint32_t(__popc(valid & ~missm));
 
-        // Ordered compaction of the misses into (id << 16 | position) keys.
-        int ng = 0;
-        int off = block_excl_scan(m_local, sScrA, &ng);
-#pragma unroll
-        for (int e = 0; e < IPT; ++e)
-            if (valid[e] && slot[e] < 0)
-                sKey[off++] = (uint64_t(uint32_t(x[e])) << 16) | uint64_t(i0 + e);
-        if (tid == 0) a.n_miss[tok] = ng;
+        int ng, idlo, idhi;
+        block_sum_min_max<T>(m_local, lo_local, hi_local, sMM, &ng, &idlo, &idhi);
+        ng = min(ng, K);
         c_miss += uint32_t(ng);
-        __syncthreads();
-        if (ng == 0) continue;
 
-        // --- Misses in ascending id (sort only if not already ascending) ---
-        int unsorted = 0;
-        for (int r = tid; r + 1 < ng; r += T) unsorted |= sKey[r] > sKey[r + 1];
-        {
-            const uint64_t bal = __ballot(unsorted);
-            if (lane == 0 && bal) sMisc[0] = 1;  // cleared below after use
+        // --- Rank of each miss among the token's misses, ascending id ------
+        int32_t rank[IPT];
+#pragma unroll
+        for (int e = 0; e < IPT; ++e) rank[e] = -1;
+        if (ng > 0) {
+            const uint32_t span = uint32_t(idhi) - uint32_t(idlo) + 1u;  // ids >= 0
+            bool fast = span <= uint32_t(lay.bitmap_words) * 32u;
+            if (fast) {
+                const int nw4 = int(((span + 31u) >> 5) + 3) & ~3;  // words, multiple of 4
+                for (int k = tid; k < (nw4 >> 2); k += T)
+                    reinterpret_cast<uint4*>(sBits)[k] = make_uint4(0, 0, 0, 0);
+                if (tid == 0) sMisc[0] = 0;
+                __syncthreads();
+                bool dup = false;
+#pragma unroll
+                for (int e = 0; e < IPT; ++e) {
+                    if (missm & (1u << e)) {
+                        const uint32_t bit = uint32_t(x[e] - idlo);
+                        const uint32_t m = 1u << (bit & 31u);
+                        dup |= (atomicOr(&sBits[bit >> 5], m) & m) != 0u;
+                    }
+                }
+                if (__ballot(dup) != 0ull && lane == 0) sMisc[0] = 1;
+                __syncthreads();
+                fast = sMisc[0] == 0;
+                if (fast) {
+                    // Prefix popcounts over the words, as uint16 (ng <= 8192),
+                    // four words per step.
+                    const int wpt = ((nw4 >> 2) + T - 1) / T * 4;
+                    const int w0 = min(tid * wpt, nw4), w1 = min(w0 + wpt, nw4);
+                    int cnt = 0;
+                    for (int k = w0; k < w1; k += 4) {
+                        const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
+                        cnt += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
+                    }
+                    int tot;
+                    int run = block_excl_scan<T>(cnt, sS0, &tot);
+                    for (int k = w0; k < w1; k += 4) {
+                        const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
+                        const uint32_t p0 = uint32_t(run);
+                        const uint32_t p1 = p0 + __popc(q.x);
+                        const uint32_t p2 = p1 + __popc(q.y);
+                        const uint32_t p3 = p2 + __popc(q.z);
+                        run = int(p3 + __popc(q.w));
+                        *reinterpret_cast<uint2*>(sPre + k) =
+                            make_uint2(p0 | (p1 << 16), p2 | (p3 << 16));
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int e = 0; e < IPT; ++e) {
+                        if (missm & (1u << e)) {
+                            const uint32_t bit = uint32_t(x[e] - idlo);
+                            const uint32_t wd = sBits[bit >> 5];
+                            rank[e] = int(sPre[bit >> 5]) +
+                                      __popc(wd & ((1u << (bit & 31u)) - 1u));
+                        }
+                    }
+                }
+            }
+            if (!fast) {
+                // General order: bitonic sort of (id << 16 | position) keys.
+                int tot;
+                int off = block_excl_scan<T>(m_local, sS1, &tot);
+#pragma unroll
+                for (int e = 0; e < IPT; ++e)
+                    if (missm & (1u << e))
+                        sKey[off++] = (uint64_t(uint32_t(x[e])) << 16) | uint64_t(i0 + e);
+                const int P = next_pow2(ng);
+                for (int r = ng + tid; r < P; r += T) sKey[r] = ~uint64_t(0);
+                __syncthreads();
+                bitonic_sort<T>(sKey, P);
+                for (int r = tid; r < ng; r += T) {
+                    const uint64_t k = sKey[r];
+                    sRank[int(k & 0xFFFFu)] = uint16_t(r);
+                    if (r + 1 < ng && (k >> 16) == (sKey[r + 1] >> 16)) c_err |= 2u;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < IPT; ++e)
+                    if (missm & (1u << e)) rank[e] = int(sRank[i0 + e]);
+            }
         }
-        __syncthreads();
-        const bool need_sort = sMisc[0] != 0;
-        if (need_sort) {
-            const int P = next_pow2(ng);
-            for (int r = ng + tid; r < P; r += T) sKey[r] = ~uint64_t(0);
+
+        if (ng > 0) {
+            // --- Pass 3: victims ---------------------------------------------
+            // Dead slots now; if fewer than ng, the least extra decay k* with
+            // #{F < k*} >= ng, applied to every slot.
+            uint32_t gw[kMaxLifeWords];
+#pragma unroll
+            for (int q = 0; q < kMaxLifeWords; ++q) gw[q] = q < dwn ? sGw[dw0 + q] : ~0u;
+            int dead_local = 0;
+#pragma unroll
+            for (int q = 0; q < kMaxLifeWords; ++q) dead_local += __popc(zero_bytes(gw[q]));
+            int dead_total;
+            int doff = block_excl_scan<T>(dead_local, sS0, &dead_total);
+            if (dead_total < ng) {
+                // Histogram of G over 16 LDS copies (lane % 16 picks one).
+                int32_t* hc = sHist + (lane & (kHistCopies - 1)) * HB;
+#pragma unroll
+                for (int q = 0; q < kMaxLifeWords; ++q) {
+                    if (q < dwn) {
+                        atomicAdd(&hc[gw[q] & 0xFFu], 1);
+                        atomicAdd(&hc[(gw[q] >> 8) & 0xFFu], 1);
+                        atomicAdd(&hc[(gw[q] >> 16) & 0xFFu], 1);
+                        atomicAdd(&hc[gw[q] >> 24], 1);
+                    }
+                }
+                __syncthreads();
+                if (tid < 64) {
+                    // k* = least k with #{F < k} = #{G <= k} >= ng.
+                    int carry = 0, kstar = -1;
+                    for (int base = 0; base < HB && kstar < 0; base += 64) {
+                        const int k = base + lane;
+                        int hv = 0;
+                        if (k < HB)
+                            for (int c = 0; c < kHistCopies; ++c) hv += sHist[c * HB + k];
+                        const int cum = wave_scan_add(hv) + carry;
+                        const uint64_t reach = __ballot(k < HB && cum >= ng);
+                        if (reach) kstar = base + __ffsll((unsigned long long)reach) - 1;
+                        carry = lane63(cum);
+                    }
+                    if (lane == 0) sMisc[1] = kstar < 0 ? L + 1 : kstar;
+                }
+                __syncthreads();
+                const uint32_t kstar = uint32_t(sMisc[1]);
+                dead_local = 0;
+#pragma unroll
+                for (int q = 0; q < kMaxLifeWords; ++q) {
+                    if (q < dwn) {
+                        uint32_t r = 0;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t v = (gw[q] >> (8 * j)) & 0xFFu;
+                            r |= (v > kstar ? v - kstar : 0u) << (8 * j);
+                        }
+                        gw[q] = r;
+                        sGw[dw0 + q] = r;
+                        dead_local += __popc(zero_bytes(r));
+                    }
+                }
+                doff = block_excl_scan<T>(dead_local, sS1, &dead_total);
+            }
+            // CollectDead: the ng lowest-index dead slots, in slot order.
+#pragma unroll
+            for (int q = 0; q < kMaxLifeWords; ++q) {
+                if (q < dwn && doff < ng) {
+                    uint32_t z = zero_bytes(gw[q]);
+                    while (z && doff < ng) {
+                        const int j = (__ffs(int(z)) - 1) >> 3;
+                        sVict[doff++] = (dw0 + q) * 4 + j;
+                        z &= z - 1u;
+                    }
+                }
+            }
             __syncthreads();
-            if (tid == 0) sMisc[0] = 0;
-            bitonic_sort(sKey, P);
-        }
-        for (int r = tid; r + 1 < ng; r += T)
-            if ((sKey[r] >> 16) == (sKey[r + 1] >> 16)) c_err |= 2u;
 
-        // --- Pass 3: least extra decay k* leaving ng dead slots ------------
-        // Histogram of lifetimes over bins F+1 in [0, L+1], one wave-
-        // aggregated LDS atomic per distinct bin per wave.
-        for (int e = 0; e < E; ++e) {
-            const int v = has_slots ? int(sF[j0 + e]) + 1 : -1;
-            uint64_t active = __ballot(v >= 0);
-            while (active) {
-                const int leader = __ffsll((unsigned long long)active) - 1;
-                const int bin = __shfl(v, leader, 64);
-                const uint64_t m = __ballot(v == bin) & active;
-                if (lane == leader) atomicAdd(&sHist[bin], __popcll(m));
-                active &= ~m;
-            }
-        }
-        __syncthreads();
-        if (tid < 64) {
-            // k* = least k with #{F < k} = sum(hist[0..k]) >= ng.
-            int carry = 0, kstar = -1;
-            for (int base = 0; base < L + 2 && kstar < 0; base += 64) {
-                const int k = base + lane;
-                const int hv = k < L + 2 ? sHist[k] : 0;
-                const int cum = wave_incl_scan(hv) + carry;
-                const uint64_t reach = __ballot(k < L + 2 && cum >= ng);
-                if (reach) kstar = base + __ffsll((unsigned long long)reach) - 1;
-                carry = __shfl(cum, 63, 64);
-            }
-            if (lane == 0) sMisc[1] = kstar < 0 ? L + 1 : kstar;
-        }
-        __syncthreads();
-        const int kstar = sMisc[1];
-
-        // Decay by k*, then CollectDead: the ng lowest-index dead slots.
-        int dead_local = 0;
-        if (has_slots) {
-            for (int e = 0; e < E; ++e) {
-                int f = sF[j0 + e];
-                if (kstar) {
-                    f = max(f - kstar, -1);
-                    sF[j0 + e] = int8_t(f);
-                }
-                dead_local += f == -1;
-            }
-        }
-        int dead_total = 0;
-        int doff = block_excl_scan(dead_local, sScrB, &dead_total);
-        if (has_slots && doff < ng) {
-            for (int e = 0; e < E && doff < ng; ++e)
-                if (sF[j0 + e] == -1) sVict[doff++] = j0 + e;
-        }
-        __syncthreads();
-
-        // Install the r-th smallest miss into the r-th victim.
-        for (int r = tid; r < ng; r += T) {
-            const uint64_t key = sKey[r];
-            const int32_t xv = int32_t(key >> 16);
-            const int i = int(key & 0xFFFFu);
-            const int32_t v = sVict[r];
-            if (sC[v] >= 0) ++c_live;
-            sC[v] = xv;
-            sF[v] = int8_t(L);
-            O[i] = v;
-            H[i] = 0;
-            reinterpret_cast<int2*>(a.pairs)[tok * K + r] = make_int2(xv, v);
-        }
-        __syncthreads();
-
-        // Link: first reusable bucket in R+1 rounds, judged on the bucket
-        // words before this token's writes and the slots after its installs.
-        int32_t tgt[IPT];
+            // --- Install the r-th smallest miss into the r-th victim ---------
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int r = tid + k * T;
-            tgt[k] = -1;
-            if (r < ng) {
-                const uint32_t xv = uint32_t(sKey[r] >> 16);
-                uint32_t p = home_bucket(xv, a.a1, smask);
-                const uint32_t d = stride_of(xv, a.a2, smask);
-                for (int t = 0; t <= R; ++t) {
-                    const int32_t wd = sQ[p];
-                    bool reusable = wd == kEmpty;
-                    if (!reusable) {
-                        const int32_t cached = sC[wd & int32_t(smask)];
-                        reusable = cached == -1 || fp_of(uint32_t(cached), a.afp) != (wd >> 16);
-                    }
-                    if (reusable) {
-                        tgt[k] = int32_t(p);
-                        break;
-                    }
-                    p = (p + d) & smask;
-                }
-                if (tgt[k] < 0) ++c_lexh;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < IPT; ++k)
-            if (tgt[k] >= 0) sQ[tgt[k]] = kClaimBase;
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < IPT; ++k)
-            if (tgt[k] >= 0) atomicMax(&sQ[tgt[k]], kClaimBase + 1 + tid + k * T);
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            if (tgt[k] >= 0) {
-                const int r = tid + k * T;
-                if (sQ[tgt[k]] == kClaimBase + 1 + r) {
-                    const uint32_t xv = uint32_t(sKey[r] >> 16);
-                    sQ[tgt[k]] = (fp_of(xv, a.afp) << 16) | sVict[r];
-                } else {
-                    ++c_lcol;
+            for (int e = 0; e < IPT; ++e) {
+                if (missm & (1u << e)) {
+                    const int r = min(max(rank[e], 0), ng - 1);
+                    const int32_t v = sVict[r];
+                    if (sC[v] >= 0) ++c_live;
+                    sC[v] = x[e];
+                    sG[v] = uint8_t(L + 1);
+                    slot[e] = v;
+                    sPair[r] = make_int2(x[e], v);
                 }
             }
+            __syncthreads();
+
+            // --- Link: first reusable bucket in R+1 rounds, judged on the
+            // bucket words before this token's writes and the slots after its
+            // installs; one scatter, the largest rank keeps a contested bucket.
+            int32_t tgt[IPT];
+            uint32_t lp[IPT], ld[IPT];
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) {
+                tgt[e] = -1;
+                lp[e] = home_bucket(uint32_t(x[e]), a.a1, smask);
+                ld[e] = stride_of(uint32_t(x[e]), a.a2, smask);
+            }
+            uint32_t search = missm;
+            for (int t = 0; t <= R; ++t) {
+                if (__ballot(search != 0u) == 0ull) break;
+                int32_t wd[IPT], cc[IPT];
+#pragma unroll
+                for (int e = 0; e < IPT; ++e) wd[e] = ((search >> e) & 1u) ? sQ[lp[e]] : kEmpty;
+#pragma unroll
+                for (int e = 0; e < IPT; ++e) cc[e] = wd[e] != kEmpty ? sC[wd[e] & int32_t(smask)] : -1;
+#pragma unroll
+                for (int e = 0; e < IPT; ++e) {
+                    const bool reusable = wd[e] == kEmpty || cc[e] == -1 ||
+                                          fp_of(uint32_t(cc[e]), a.afp) != (wd[e] >> 16);
+                    const bool take = ((search >> e) & 1u) && reusable;
+                    tgt[e] = take ? int32_t(lp[e]) : tgt[e];
+                    search &= ~(uint32_t(take) << e);
+                    lp[e] = (lp[e] + ld[e]) & smask;
+                }
+            }
+            c_lexh += uint32_t(__popc(search));
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < IPT; ++e)
+                if (tgt[e] >= 0) sQ[tgt[e]] = kClaimBase;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < IPT; ++e)
+                if (tgt[e] >= 0) atomicMax(&sQ[tgt[e]], kClaimBase + 1 + rank[e]);
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) {
+                if (tgt[e] >= 0) {
+                    if (sQ[tgt[e]] == kClaimBase + 1 + rank[e])
+                        sQ[tgt[e]] = (fp_of(uint32_t(x[e]), a.afp) << 16) | slot[e];
+                    else
+                        ++c_lcol;
+                }
+            }
+
+            // Miss list (id, slot) in rank order.
+            int2* P = reinterpret_cast<int2*>(a.pairs) + tok * K;
+            for (int r = tid; r < ng; r += T) P[r] = sPair[r];
         }
+
+        // Slot table and hit mask of this thread's positions.
+        int32_t o[IPT];
+        int8_t hm[IPT];
+#pragma unroll
+        for (int e = 0; e < IPT; ++e) {
+            const bool ok = (valid >> e) & 1u;
+            o[e] = ok ? slot[e] : -1;
+            hm[e] = ok ? int8_t(((missm >> e) & 1u) ? 0 : 1) : int8_t(-1);
+        }
+        store_outputs<IPT>(O, H, i0, K, vec, o, hm);
+        if (tid == 0) a.n_miss[tok] = ng;
         __syncthreads();
     }
 
     // End of step: empty every slot caching a speculative id (>= N), then
-    // write the state back (lifetimes widened to int32).
+    // write the state back (F = G - 1).
     for (int j = tid; j < (S >> 2); j += T) {
         int4 c = reinterpret_cast<const int4*>(sC)[j];
         if (c.x >= N) c.x = -1;
@@ -375,20 +615,21 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         if (c.w >= N) c.w = -1;
         reinterpret_cast<int4*>(gC)[j] = c;
         reinterpret_cast<int4*>(gQ)[j] = reinterpret_cast<const int4*>(sQ)[j];
-        const char4 f8 = reinterpret_cast<const char4*>(sF)[j];
-        reinterpret_cast<int4*>(gF)[j] = make_int4(f8.x, f8.y, f8.z, f8.w);
+        const uint32_t w = sGw[j];
+        reinterpret_cast<int4*>(gF)[j] =
+            make_int4(int(w & 0xFFu) - 1, int((w >> 8) & 0xFFu) - 1,
+                      int((w >> 16) & 0xFFu) - 1, int(w >> 24) - 1);
     }
 
     // Counters: wave sums, then one LDS atomic per wave and counter.
-    int32_t* sCnt = sScrA + 64;  // sMisc area, 8 ints
-    __syncthreads();
+    int32_t* sCnt = sMisc + 2;
     if (tid < 8) sCnt[tid] = 0;
     __syncthreads();
     const uint32_t vals[6] = {c_hits, c_look, c_lcol, c_lexh, c_live, c_visit};
     const int idx[6] = {0, 1, 3, 4, 5, 7};
 #pragma unroll
     for (int k = 0; k < 6; ++k) {
-        const int s = wave_sum(int(vals[k]));
+        const int s = lane63(wave_scan_add(int(vals[k])));
         if (lane == 0 && s) atomicAdd(&sCnt[idx[k]], s);
     }
     const uint64_t e1 = __ballot(c_err & 1u), e2 = __ballot(c_err & 2u);
@@ -398,41 +639,64 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         int32_t* cnt = a.CNT + size_t(b) * 8;
         const uint32_t add = tid == 2 ? c_miss : uint32_t(sCnt[tid]);
         if (tid == 6)
-            cnt[6] = cnt[6] | int32_t(add);
+            cnt[6] = cnt_old | int32_t(add);
         else
-            cnt[tid] = int32_t(uint32_t(cnt[tid]) + add);
+            cnt[tid] = int32_t(uint32_t(cnt_old) + add);
     }
 }
 
-template <int IPT>
-hipError_t launch_ipt(const Stage1Args& a, size_t lds, hipStream_t s) {
-    hipLaunchKernelGGL(stage1_kernel<IPT>, dim3(a.B), dim3(T), lds, s, a);
+template <int T, int IPT>
+hipError_t launch_one(const Stage1Args& a, size_t lds, hipStream_t s) {
+    hipLaunchKernelGGL((stage1_kernel<T, IPT>), dim3(a.B), dim3(T), lds, s, a);
     return hipGetLastError();
+}
+
+template <int T, int IPT>
+hipError_t prepare_one(size_t lds) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<T, IPT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
 }
 
 }  // namespace
 
-hipError_t stage1_prepare(size_t lds_bytes) {
-    hipError_t e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<1>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<2>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<4>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<8>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
+int stage1_threads(int K, int requested) {
+    if (requested) return requested;
+    // Two ids per thread up to 1024 threads: the probe and link rounds are
+    // LDS-latency bound, and more waves hide more of it (measured on the
+    // matching and residency shapes: 1024 threads beat 512 and 256).
+    const int half = next_pow2(K) / 2;
+    return half <= 256 ? 256 : half >= 1024 ? 1024 : half;
 }
 
-hipError_t launch_stage1(const Stage1Args& a, size_t lds, hipStream_t s) {
+template <int T>
+hipError_t prepare_t(size_t lds) {
+    hipError_t e;
+    if ((e = prepare_one<T, 1>(lds)) != hipSuccess) return e;
+    if ((e = prepare_one<T, 2>(lds)) != hipSuccess) return e;
+    if ((e = prepare_one<T, 4>(lds)) != hipSuccess) return e;
+    return prepare_one<T, 8>(lds);
+}
+
+hipError_t stage1_prepare(size_t lds) {
+    hipError_t e;
+    if ((e = prepare_t<256>(lds)) != hipSuccess) return e;
+    if ((e = prepare_t<512>(lds)) != hipSuccess) return e;
+    return prepare_t<1024>(lds);
+}
+
+template <int T>
+hipError_t launch_t(const Stage1Args& a, size_t lds, hipStream_t s) {
     const int ipt = (a.K + T - 1) / T;
-    if (ipt <= 1) return launch_ipt<1>(a, lds, s);
-    if (ipt <= 2) return launch_ipt<2>(a, lds, s);
-    if (ipt <= 4) return launch_ipt<4>(a, lds, s);
-    return launch_ipt<8>(a, lds, s);
+    if (ipt <= 1) return launch_one<T, 1>(a, lds, s);
+    if (ipt <= 2) return launch_one<T, 2>(a, lds, s);
+    if (ipt <= 4) return launch_one<T, 4>(a, lds, s);
+    return launch_one<T, 8>(a, lds, s);
+}
+
+hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds, hipStream_t s) {
+    if (threads == 256) return launch_t<256>(a, lds, s);
+    if (threads == 512) return launch_t<512>(a, lds, s);
+    return launch_t<1024>(a, lds, s);
 }
 
 }  // namespace avsg

@@ -20,16 +20,17 @@ def say(msg):
     sys.stdout.flush()
 
 
-def make_cfg(r, w, flags=0, gather_blocks=0):
+def make_cfg(r, w, flags=0, gather_blocks=0, stage1_threads=0):
     return r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
                                  a1=w.a1, a2=w.a2, a_fp=w.afp, flags=flags,
-                                 gather_blocks=gather_blocks)
+                                 gather_blocks=gather_blocks,
+                                 stage1_threads=stage1_threads)
 
 
 class Pair:
     """A GPU handle and an oracle on one workload."""
 
-    def __init__(self, w, gather=True, gather_blocks=0, shadow=True):
+    def __init__(self, w, gather=True, gather_blocks=0, shadow=True, stage1_threads=0):
         import torch
         import recall_step_amd as r
         self.r, self.torch, self.w = r, torch, w
@@ -38,8 +39,8 @@ class Pair:
         if gather:
             w.fill_host_kv(self.host.array)
         flags = 0 if gather else r.FLAG_SKIP_GATHER
-        self.rs = r.RecallStep(make_cfg(r, w, flags, gather_blocks), self.host,
-                               w.host_rows_total)
+        self.rs = r.RecallStep(make_cfg(r, w, flags, gather_blocks, stage1_threads),
+                               self.host, w.host_rows_total)
         self.oracle = Oracle.for_workload(
             w, host_kv=self.host.array if gather else None, shadow=shadow and gather)
         dev = self.rs.Q.device
@@ -88,12 +89,15 @@ class Pair:
             self.host.close()
 
 
-def run_parity(w, steps=None, kv_every=None, gather=True, gather_blocks=0, label=None):
+def run_parity(w, steps=None, kv_every=None, gather=True, gather_blocks=0, label=None,
+               stage1_threads=0):
+    """Step both sides through w, comparing everything after every step;
+    returns the oracle's counters, int64 [B][8]."""
     label = label or w.name
     steps = w.steps if steps is None else steps
     say(f"[parity] {label}: B={w.B} Nq={w.Nq} K={w.K} S={w.S} L={w.L} R={w.R} "
         f"row={w.row_bytes} host_rows={w.host_rows_total} steps={steps} gather={gather}")
-    p = Pair(w, gather=gather, gather_blocks=gather_blocks)
+    p = Pair(w, gather=gather, gather_blocks=gather_blocks, stage1_threads=stage1_threads)
     try:
         for t in range(steps):
             p.gpu_step(t)
@@ -101,6 +105,6 @@ def run_parity(w, steps=None, kv_every=None, gather=True, gather_blocks=0, label
             last = t == steps - 1
             check_kv = gather and (last or (kv_every is not None and t % kv_every == 0))
             p.compare(ref, f"{label} step {t}", check_kv=check_kv)
-        return p.oracle.CNT.astype(np.int64).sum(0)
+        return p.oracle.CNT.astype(np.int64)
     finally:
         p.close()

@@ -38,7 +38,7 @@ def test_config_default_values():
     c = r.avsg_config_default(8, 1, 2048, 2048, 1280)
     assert (c.B, c.N_q, c.K, c.S, c.row_bytes) == (8, 1, 2048, 2048, 1280)
     assert (c.L, c.R, c.a1, c.a2, c.a_fp) == (15, 7, 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D)
-    assert (c.flags, c.gather_blocks) == (0, 0)
+    assert (c.flags, c.gather_blocks, c.stage1_threads) == (0, 0, 0)
     assert r.avsg_validate_config(c) == 0
 
 
@@ -46,7 +46,8 @@ def test_config_default_values():
     ("S", 3000), ("S", 8), ("S", 131072), ("K", 0), ("K", 4096), ("B", 0),
     ("N_q", 0), ("L", 0), ("L", 128), ("R", -1), ("a1", 2), ("a2", 4),
     ("a_fp", 0), ("row_bytes", 1000), ("row_bytes", 0), ("flags", 8),
-    ("gather_blocks", -1)])
+    ("gather_blocks", -1), ("stage1_threads", 128), ("stage1_threads", 300),
+    ("stage1_threads", 2048)])
 def test_invalid_configs_rejected(field, value):
     c = r.avsg_config_default(4, 1, 2048, 2048, 1280)
     setattr(c, field, value)
@@ -61,12 +62,20 @@ def test_capacity_bound_enforced():
 
 def test_lds_and_workspace_sizes():
     c = r.avsg_config_default(32, 1, 2048, 8192, 1280)
-    # 9 bytes per slot (two int32 arrays + int8 lifetimes) + 8 B per sort key
-    # + 4 B per victim + histogram + scratch.
+    # 9 bytes per slot (two int32 arrays + int8 lifetimes) + 4 B per victim +
+    # a miss-rank bitmap over 2^18 ids with uint16 prefix counts per word
+    # (6 B per 32 ids, larger than the 8 B per sort key of the fallback) +
+    # 16 copies of the (L+2)-bin lifetime histogram + scratch.
     lds = r.avsg_stage1_lds_bytes(c)
-    assert 9 * 8192 + 8 * 2048 + 4 * 2048 <= lds <= 9 * 8192 + 8 * 2048 + 4 * 2048 + 1024
+    base = 9 * 8192 + 4 * 2048 + 6 * (1 << 18) // 32 + 16 * (15 + 2) * 4
+    assert base <= lds <= base + 1024
     assert lds <= 160 * 1024
     assert r.avsg_workspace_bytes(c) == 32 * 1 * 2048 * 2 * 4
+    # K = S = 8192 cannot be staged in 160 KiB: reported as 0 (unsupported).
+    assert r.avsg_stage1_lds_bytes(r.avsg_config_default(1, 1, 8192, 8192, 1280)) == 0
+    for K, S in [(1, 16), (256, 512), (2048, 2048), (4096, 8192), (256, 16384)]:
+        lds = r.avsg_stage1_lds_bytes(r.avsg_config_default(1, 1, K, S, 1280))
+        assert 9 * S + 4 * K + 8 * K <= lds <= 160 * 1024
 
 
 def test_create_rejects_bad_arguments_before_touching_a_device():

@@ -35,7 +35,7 @@ def test_fuzz_corpus(chunk):
 
 
 def test_tiny_full():
-    cnt = run_parity(make("tiny"), kv_every=1)
+    cnt = run_parity(make("tiny"), kv_every=1).sum(0)
     assert cnt[1] == 16 * 256
 
 
@@ -45,7 +45,7 @@ def test_matching_full():
 
 def test_mtp3_full():
     cnt = run_parity(make("mtp3"), kv_every=8)
-    assert cnt[6] == 0
+    assert (cnt[:, 6] == 0).all()
 
 
 def test_imbalanced_full():
@@ -57,9 +57,11 @@ def test_residency_full():
 
 
 @pytest.mark.parametrize("K,S", [(256, 512), (1000, 1024), (2048, 2048), (3000, 4096),
-                                 (4096, 8192), (1, 16), (64, 64)])
+                                 (4096, 8192), (1, 16), (64, 64), (1501, 2048),
+                                 (2999, 4096), (4095, 8192)])
 def test_shape_sweep_stage_one(K, S):
-    """Ragged and maximal K, several S: every IPT template and slot-per-thread
+    """Ragged and maximal K, several S: every IPT template, the scalar path
+    for K not a multiple of the ids per thread, and every slot-per-thread
     split of the Stage-One kernel, without the copy."""
     w = make("matching", steps=4)
     rng = np.random.default_rng([K, S])
@@ -72,6 +74,69 @@ def test_shape_sweep_stage_one(K, S):
     w.ctx_len = w.ctx_len[:4, :2]
     w.host_rows, w.row_base = w.host_rows[:2], w.row_base[:2]
     run_parity(w, gather=False, label=f"sweep K={K} S={S}")
+
+
+def _stage_one_only(name, K, S, steps, B, host_rows, draw):
+    """A Stage-One-only workload whose selections come from draw(rng, t, b)."""
+    w = make("matching", steps=steps)
+    rng = np.random.default_rng([K, S, steps, B])
+    topk = np.full((steps, B, 1, K), -1, np.int32)
+    for t in range(steps):
+        for b in range(B):
+            ids = draw(rng, t, b)
+            topk[t, b, 0, :ids.size] = ids
+    w.name, w.topk, w.B, w.K, w.S, w.steps = name, topk, B, K, S, steps
+    w.ctx_len = np.full((steps, B), host_rows, np.int32)
+    w.host_rows = np.full(B, host_rows, np.int32)
+    w.row_base = np.arange(B, dtype=np.int64) * host_rows
+    return w
+
+
+def test_wide_id_span_takes_the_sorting_path():
+    """Misses spread over ids up to 2^30 exceed the rank bitmap's 2^18-id
+    window, so those tokens order their misses by sorting; every other step
+    keeps half of the previous selection, so hits and evictions occur too."""
+    prev = {}
+
+    def draw(rng, t, b):
+        K = 2048
+        if t % 2 == 1 and b in prev:
+            keep = rng.choice(prev[b], K // 2, replace=False)
+            fresh = rng.choice(1 << 30, K, replace=False)
+            fresh = np.setdiff1d(fresh, keep)[: K - keep.size]
+            ids = np.concatenate([keep, rng.permutation(fresh)])
+        elif t % 3 == 2:
+            ids = rng.choice(1 << 17, K, replace=False)    # narrow span
+        else:
+            ids = rng.choice(1 << 30, K, replace=False)
+        prev[b] = ids.astype(np.int32)
+        return rng.permutation(ids).astype(np.int32)
+
+    w = _stage_one_only("wide span", 2048, 4096, 8, 3, 1 << 30, draw)
+    cnt = run_parity(w, gather=False).sum(0)
+    assert cnt[0] > 0 and cnt[5] > 0
+
+
+def test_repeated_missing_ids_take_the_sorting_path():
+    """A token that misses the same id twice: both copies get slots in
+    (id, position) order and the duplicate error bit is set."""
+    def draw(rng, t, b):
+        ids = rng.choice(50000, 700, replace=False)
+        dup = rng.choice(ids, 20, replace=False)
+        return rng.permutation(np.concatenate([ids, dup])).astype(np.int32)
+
+    w = _stage_one_only("repeated ids", 720, 2048, 5, 2, 50000, draw)
+    cnt = run_parity(w, gather=False)
+    assert (cnt[:, 6] & 2).all()
+
+
+@pytest.mark.parametrize("threads", [256, 512, 1024])
+@pytest.mark.parametrize("name", ["matching", "mtp3"])
+def test_stage_one_workgroup_size_does_not_change_results(name, threads):
+    """Every Stage-One workgroup size (ids per thread 8 down to 1 at K =
+    2048) gives the oracle's results."""
+    w = make(name, steps=6) if name == "matching" else make(name, steps=6, B=4)
+    run_parity(w, gather=False, stage1_threads=threads, label=f"{name} T={threads}")
 
 
 def test_state_beyond_lds_is_unsupported():
