@@ -51,6 +51,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--stage1-threads", type=int, default=0)
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="instead of the step benchmark: Stage-One throughput on the "
+                         "residency request shape (K=2048, S=8192) at B = 32..512, "
+                         "one JSON line per batch size")
     return ap.parse_args()
 
 
@@ -80,6 +85,81 @@ def pinned_h2d_peak(r, torch, stream, nbytes=1 << 30, reps=10):
     del dst
     pool.close()
     return best
+
+
+def hbm_copy_peak(torch, stream, nbytes=1 << 30, reps=5):
+    """Best-of-N device-to-device copy of nbytes (torch's copy kernel), as
+    HBM GB/s counting the read and the write."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    best = 0.0
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            e1.synchronize()
+            best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+def stage1_algorithmic_bytes(B, S, Nq, lookups, visits, misses):
+    """Stage-One algorithmic HBM bytes of one step: lifetimes read and written
+    once per request (2*S*4 B), 4 B id in + 4 B slot out + 1 B mask out per
+    lookup, 8 B (word + cached id) per bucket visited, 20 B per miss (install
+    12 B + miss list 8 B), 4 B count per token."""
+    return B * 2 * S * 4 + lookups * 9 + visits * 8 + misses * 20 + B * Nq * 4
+
+
+def probe_sweep(args):
+    import torch
+    import recall_step_amd as r
+    from workloads import make
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    for B in (32, 128, 256, 512):
+        w = make("residency", steps=16, B=B)
+        cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
+                                    a1=w.a1, a2=w.a2, a_fp=w.afp, flags=r.FLAG_SKIP_GATHER,
+                                    stage1_threads=args.stage1_threads)
+        rs = r.RecallStep(cfg, None, w.host_rows_total, stream=stream)
+        topk = torch.from_numpy(np.ascontiguousarray(w.topk)).cuda()
+        ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).cuda()
+        row_base = torch.from_numpy(w.row_base).cuda()
+        host_rows = torch.from_numpy(w.host_rows).cuda()
+        ios = [rs.io(topk[t], ctx[t], row_base, host_rows) for t in range(w.steps)]
+        torch.cuda.synchronize()
+        for t in range(8):
+            r.avsg_match(rs.handle, ios[t], sh)
+        torch.cuda.synchronize()
+        cnt0 = rs.CNT.cpu().numpy().astype(np.int64)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(8, 16):
+            r.avsg_match(rs.handle, ios[t], sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        d = (rs.CNT.cpu().numpy().astype(np.int64) - cnt0).sum(0)
+        us = e0.elapsed_time(e1) * 1e3 / 8
+        per_step = stage1_algorithmic_bytes(B, w.S, w.Nq, d[r.CNT_LOOKUPS] / 8,
+                                            d[r.CNT_PROBE_VISITS] / 8, d[r.CNT_MISSES] / 8)
+        staged = B * (2 * 3 * w.S * 4 + w.Nq * w.K * 9)  # Q, C, F in and out + ids/outputs
+        gbps = per_step / (us * 1e-6) / 1e9
+        print(json.dumps({
+            "probe_sweep": "residency request shape, Stage One only",
+            "B": B, "K": w.K, "S": w.S, "stage1_us": round(us, 2),
+            "match_Mkeys_per_s": round(d[r.CNT_LOOKUPS] / 8 / us, 1),
+            "algorithmic_bytes_per_step": int(per_step),
+            "achieved_GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "state_traffic_GBps": round(staged / (us * 1e-6) / 1e9, 1),
+            "hit_rate": round(d[r.CNT_HITS] / d[r.CNT_LOOKUPS], 4)}), flush=True)
+        rs.close()
+    return 0
 
 
 def contiguous_gather_peak(r, torch, stream, row_bytes=1280, rows=1 << 19, blocks=0):
@@ -143,6 +223,8 @@ def main():
               f"with no exchange between GPUs, and this build measures one GPU's "
               f"share; --gpus {args.gpus} is not supported.", file=sys.stderr)
         return 2
+    if args.probe_sweep:
+        return probe_sweep(args)
     import torch
     import recall_step_amd as r
     from workloads import make
@@ -156,7 +238,8 @@ def main():
     w.fill_host_kv(host.array)
     cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
                                 a1=w.a1, a2=w.a2, a_fp=w.afp,
-                                gather_blocks=args.gather_blocks)
+                                gather_blocks=args.gather_blocks,
+                                stage1_threads=args.stage1_threads)
     rs = r.RecallStep(cfg, host, w.host_rows_total, stream=stream)
     topk = torch.from_numpy(np.ascontiguousarray(w.topk)).cuda()
     ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).cuda()
@@ -199,12 +282,8 @@ def main():
     gather_gbps = gather_bytes / (sum(g_ms) * 1e-3) / 1e9
     mkeys = lookups / (sum(s1_ms) * 1e-3) / 1e6
 
-    # Stage One algorithmic HBM bytes per launch (per step): lifetimes read
-    # and written once per request (2*S*4 B), 4 B id in + 4 B slot out + 1 B
-    # mask out per lookup, 8 B (word + cached id) per bucket visited, 20 B per
-    # miss (install 12 B + miss list 8 B), 4 B count per token.
-    s1_bytes_step = (w.B * 2 * w.S * 4 + lookups / K * 9 + visits / K * 8 +
-                     misses / K * 20 + w.B * w.Nq * 4)
+    s1_bytes_step = stage1_algorithmic_bytes(w.B, w.S, w.Nq, lookups / K, visits / K,
+                                             misses / K)
 
     result = {
         "metric": METRIC,
@@ -257,6 +336,7 @@ def main():
         peak = pinned_h2d_peak(r, torch, stream)
         contig = contiguous_gather_peak(r, torch, stream, w.row_bytes,
                                         blocks=args.gather_blocks)
+        result["hbm_copy_peak_GBps"] = round(hbm_copy_peak(torch, stream), 1)
         result["pinned_h2d_memcpy_peak_GBps"] = round(peak, 2)
         result["contiguous_gather_GBps"] = round(contig, 2)
         result["gather_frac_of_memcpy_peak"] = round(gather_gbps / peak, 4)

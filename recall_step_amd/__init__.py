@@ -227,7 +227,9 @@ class RecallStep:
         self.C = torch.empty((B, S), dtype=torch.int32, device=dev)
         self.F = torch.empty((B, S), dtype=torch.int32, device=dev)
         self.CNT = torch.empty((B, 8), dtype=torch.int32, device=dev)
-        self.dev_kv = torch.zeros((B, S, cfg.row_bytes), dtype=torch.uint8, device=dev)
+        # Without the copy stage the slot buffer is never touched.
+        kv_shape = (1, 1, 16) if cfg.flags & FLAG_SKIP_GATHER else (B, S, cfg.row_bytes)
+        self.dev_kv = torch.zeros(kv_shape, dtype=torch.uint8, device=dev)
         self.slot_table = torch.empty((B, Nq, K), dtype=torch.int32, device=dev)
         self.hit_mask = torch.empty((B, Nq, K), dtype=torch.int8, device=dev)
         self.n_miss = torch.empty((B, Nq), dtype=torch.int32, device=dev)

@@ -157,7 +157,7 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** 
     h->device = dev;
     h->lds_bytes = lds;
     h->gather_blocks = cfg->gather_blocks > 0 ? cfg->gather_blocks
-                                              : 4 * prop.multiProcessorCount;
+                                              : 2 * prop.multiProcessorCount;
     h->stage1_threads = avsg::stage1_threads(cfg->K, cfg->stage1_threads);
     e = hipMalloc(reinterpret_cast<void**>(&h->ws_pairs), avsg_workspace_bytes(cfg));
     if (e != hipSuccess) {

@@ -10,11 +10,12 @@
 // device-mapped address (zero-copy loads over the host link).  Every
 // workgroup scans the per-token miss counts itself, so the total M never
 // leaves the device and the grid needs no host decision; workgroup w then
-// copies flat misses [w*M/G, (w+1)*M/G).  Rows are resolved 64 at a time into
+// copies flat misses [w*M/G, (w+1)*M/G).  Rows are resolved 256 at a time into
 // LDS (source and destination byte offsets), after which consecutive lanes
 // move consecutive 16-byte chunks of a row: one wave reads 1 KiB of a row's
 // contiguous host bytes per instruction, and each lane keeps several loads in
-// flight before storing.
+// flight before storing.  A grid of twice the CU count measured best on
+// gfx950: the host link is saturated with fewer requests queued.
 #include "internal.h"
 
 namespace avsg {
@@ -38,6 +39,9 @@ __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
     __shared__ int64_t sSrc[kGatherRowsPerPass];
     __shared__ int64_t sDst[kGatherRowsPerPass];
     __shared__ int32_t sWave[T / 64 + 1];
+
+    // An empty pool has no row to read (every miss is then out of range).
+    if (a.host_rows_total <= 0) return;
 
     const int tid = threadIdx.x;
     const int lane = __lane_id();
@@ -74,8 +78,8 @@ __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
 
     for (int64_t base = lo; base < hi; base += kGatherRowsPerPass) {
         const int nrows = int(min<int64_t>(kGatherRowsPerPass, hi - base));
-        if (tid < nrows) {
-            const int32_t m = int32_t(base + tid);
+        for (int i = tid; i < nrows; i += T) {
+            const int32_t m = int32_t(base + i);
             // Token of flat miss m: last k with sOff[k] <= m.
             int l = 0, h = ntok - 1;
             while (l < h) {
@@ -90,28 +94,32 @@ __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
             const int32_t hr = a.host_rows[bq];
             const bool ok = pr.x >= 0 && pr.x < hr && pr.y >= 0 && pr.y < a.S &&
                             rb >= 0 && rb + hr <= a.host_rows_total;
-            sSrc[tid] = ok ? (rb + pr.x) * int64_t(a.row_bytes) : int64_t(-1);
-            sDst[tid] = (int64_t(bq) * a.S + pr.y) * int64_t(a.row_bytes);
+            sSrc[i] = ok ? (rb + pr.x) * int64_t(a.row_bytes) : int64_t(-1);
+            sDst[i] = (int64_t(bq) * a.S + pr.y) * int64_t(a.row_bytes);
         }
         __syncthreads();
+        // Consecutive lanes move consecutive 16-byte chunks of a row.  The
+        // loads of an iteration are unconditional (a rejected row reads row 0
+        // of the pool, always in bounds) so all kUnroll are in flight at
+        // once; only the stores are predicated.
         const int items = nrows * cpr;
         for (int it0 = tid; it0 < items; it0 += T * kUnroll) {
             int4 v[kUnroll];
-            uint8_t* dptr[kUnroll];
+            int64_t d[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int it = it0 + u * T;
-                const int row = min(it, items - 1) / cpr;
-                const int c = min(it, items - 1) - row * cpr;
+                const int itc = min(it, items - 1);
+                const int row = itc / cpr;
+                const int c = itc - row * cpr;
                 const int64_t src = sSrc[row];
-                const bool live = it < items && src >= 0;
-                dptr[u] = live ? a.dev + sDst[row] + int64_t(c) * 16 : nullptr;
-                v[u] = live ? *reinterpret_cast<const int4*>(a.host + src + int64_t(c) * 16)
-                            : make_int4(0, 0, 0, 0);
+                v[u] = *reinterpret_cast<const int4*>(a.host + max(src, int64_t(0)) +
+                                                      int64_t(c) * 16);
+                d[u] = (it < items && src >= 0) ? sDst[row] + int64_t(c) * 16 : int64_t(-1);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                if (dptr[u]) *reinterpret_cast<int4*>(dptr[u]) = v[u];
+                if (d[u] >= 0) *reinterpret_cast<int4*>(a.dev + d[u]) = v[u];
         }
         __syncthreads();
     }

@@ -24,7 +24,7 @@ constexpr int kMaxLifeWords = 16;
 
 // Stage Two: 256-thread workgroups, rows resolved in passes of this size.
 constexpr int kGatherThreads = 256;
-constexpr int kGatherRowsPerPass = 64;
+constexpr int kGatherRowsPerPass = 256;
 // Largest B * N_q the gather prologue scans in LDS.
 constexpr int kMaxTokens = 16384;
 
