@@ -11,8 +11,12 @@ first, then the timed ones, wrapping around if more steps are asked for).
 
 Inputs are resident in HBM (selections) and in pinned host memory (the KV
 pool, which is where the method keeps it) before the timed region starts.
-Kernel durations come from HIP events recorded on the stream the kernels run
-on; the CPU oracle is timed on the host cores beside it.
+The headline step latency is the mean GPU time of one captured step (Stage
+One + gather) replayed per step, between HIP events on the stream it runs
+on; each step's ids are copied into the captured input buffers before its
+start event.  A second, eager pass with an event between the two kernels
+gives the per-kernel times, the gather bandwidth and the counters.  The CPU
+oracle is timed on the host cores beside it.
 
 Prints one JSON line.
 """
@@ -34,6 +38,41 @@ sys.path.insert(0, ROOT)
 METRIC = "recall-step latency (us) + effective host->HBM gather GB/s; match Mkeys/s"
 PCIE_GEN5_X16_GBPS = 64.0   # published per-direction peak of the host link
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+
+
+GATHER_PMC_SUMMARY = os.path.join(ROOT, "profiles", "gather_kernel.matching.pmc.txt")
+GATHER_SOURCES = [os.path.join(ROOT, "recall_step_amd", "csrc", f)
+                  for f in ("gather.hip", "internal.h")]
+
+
+def gather_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GATHER_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload):
+    """HBM-side bytes per gather launch from the committed rocprofv3 PMC
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known
+    size), or None when the summary is for another workload or for gather
+    sources other than the ones built here."""
+    if workload != "matching" or not os.path.exists(GATHER_PMC_SUMMARY):
+        return None
+    fields = {}
+    with open(GATHER_PMC_SUMMARY) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("gather_source_sha256_16") != gather_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -270,6 +309,35 @@ def main():
     wall = time.perf_counter() - t0
 
     cnt1 = rs.CNT.cpu().numpy().astype(np.int64)
+
+    # Headline: the same steps from an empty buffer as replays of one captured
+    # step (match + gather); each step's ids are copied into the captured input
+    # buffers before its start event.
+    rs.state_init(stream=stream)
+    topk_in = torch.empty_like(topk[0])
+    ctx_in = torch.empty_like(ctx[0])
+    gio = rs.io(topk_in, ctx_in, row_base, host_rows)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            rs.step(gio, stream=stream)
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+           for _ in range(args.warmup + K)]
+    torch.cuda.synchronize()
+    tg0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for k in range(args.warmup + K):
+            t = k % w.steps
+            topk_in.copy_(topk[t], non_blocking=True)
+            ctx_in.copy_(ctx[t], non_blocking=True)
+            gev[k][0].record(stream)
+            graph.replay()
+            gev[k][1].record(stream)
+    torch.cuda.synchronize()
+    graph_wall = time.perf_counter() - tg0
+    step_ms = [e[0].elapsed_time(e[1]) for e in gev[args.warmup:]]
+    del graph
     d = (cnt1 - cnt0).sum(0)
     s1_ms = [e[0].elapsed_time(e[1]) for e in ev]
     g_ms = [e[1].elapsed_time(e[2]) for e in ev]
@@ -278,7 +346,7 @@ def main():
     gather_bytes = misses * w.row_bytes
     s1_avg_s = sum(s1_ms) * 1e-3 / K
     g_avg_s = sum(g_ms) * 1e-3 / K
-    step_us = wall / K * 1e6
+    step_us = sum(step_ms) * 1e3 / K
     gather_gbps = gather_bytes / (sum(g_ms) * 1e-3) / 1e9
     mkeys = lookups / (sum(s1_ms) * 1e-3) / 1e6
 
@@ -301,6 +369,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "N_q": w.Nq, "K": w.K, "S": w.S,
                    "row_bytes": w.row_bytes, "context": int(w.host_rows.max()),
                    "L": w.L, "R": w.R, "parallelism": "single GPU"},
+        "step_us_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2) for q in (50, 90)],
+        "wall_us_per_step_with_input_copies": round(graph_wall / (args.warmup + K) * 1e6, 2),
+        "eager_wall_us_per_step": round(wall / K * 1e6, 2),
         "gather_GBps": round(gather_gbps, 2),
         "match_Mkeys_per_s": round(mkeys, 1),
         "stage1_us": round(s1_avg_s * 1e6, 2),
@@ -316,7 +387,7 @@ def main():
             "peak": PCIE_GEN5_X16_GBPS,
             "unit": "GB/s",
             "frac": round(gather_gbps / PCIE_GEN5_X16_GBPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(w.name),
             "kernel": "gather_kernel",
             "bytes_per_launch": round(gather_bytes / K),
         },
