@@ -91,6 +91,11 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--stage1-threads", type=int, default=0)
+    ap.add_argument("--ratios", action="store_true",
+                    help="instead of the step benchmark: the comparison points the "
+                         "pages measure against (gather partitions at B=1/25%% and "
+                         "B=8/75%% reuse; no-reuse KV Offload on the matching "
+                         "workload), one JSON line each")
     ap.add_argument("--probe-sweep", action="store_true",
                     help="instead of the step benchmark: Stage-One throughput on the "
                          "residency request shape (K=2048, S=8192) at B = 32..512, "
@@ -201,6 +206,86 @@ def probe_sweep(args):
     return 0
 
 
+def eager_steps(r, torch, stream, w, host, flags, warmup, steps):
+    """Run warmup + steps recall steps with an event between Stage One and
+    the gather; returns per-kernel means and the counter deltas."""
+    cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
+                                a1=w.a1, a2=w.a2, a_fp=w.afp, flags=flags)
+    rs = r.RecallStep(cfg, host, w.host_rows_total, stream=stream)
+    topk = torch.from_numpy(np.ascontiguousarray(w.topk)).cuda()
+    ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).cuda()
+    row_base = torch.from_numpy(w.row_base).cuda()
+    host_rows = torch.from_numpy(w.host_rows).cuda()
+    ios = [rs.io(topk[t], ctx[t], row_base, host_rows) for t in range(w.steps)]
+    sh = stream.cuda_stream
+    torch.cuda.synchronize()
+    for t in range(warmup):
+        r.avsg_step(rs.handle, ios[t % w.steps], sh)
+    torch.cuda.synchronize()
+    cnt0 = rs.CNT.cpu().numpy().astype(np.int64)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        io = ios[(warmup + k) % w.steps]
+        ev[k][0].record(stream)
+        r.avsg_match(rs.handle, io, sh)
+        ev[k][1].record(stream)
+        r.avsg_gather(rs.handle, io, sh)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    d = (rs.CNT.cpu().numpy().astype(np.int64) - cnt0).sum(0)
+    s1 = sum(e[0].elapsed_time(e[1]) for e in ev) * 1e3 / steps
+    g = sum(e[1].elapsed_time(e[2]) for e in ev) * 1e3 / steps
+    rs.close()
+    misses = d[r.CNT_MISSES] / steps
+    return {"stage1_us": round(s1, 2), "gather_us": round(g, 2),
+            "step_us": round(s1 + g, 2), "rows_per_step": round(misses, 1),
+            "gather_GBps": round(misses * w.row_bytes / (g * 1e-6) / 1e9, 2),
+            "hit_rate": round(d[r.CNT_HITS] / max(1, d[r.CNT_LOOKUPS]), 4)}
+
+
+def ratios(args):
+    """The pages' comparison points, measured in kind on this GPU:
+    effective H2D bandwidth of the per-row split against request-level
+    assignment (B=1, 25 % reuse) and against equal top-K partitions (B=8,
+    75 % reuse), and the recall step without reuse (KV Offload) against
+    the one with it on the matching workload."""
+    import torch
+    import recall_step_amd as r
+    from workloads import make
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    parts = {"per_row": 0, "by_request": r.FLAG_GATHER_BY_REQUEST,
+             "by_topk": r.FLAG_GATHER_BY_TOPK}
+    for name, pct, other in (("reuse25_b1", 25, "by_request"), ("reuse75_b8", 75, "by_topk")):
+        w = make(name)
+        host = r.HostPool(w.host_bytes)
+        w.fill_host_kv(host.array)
+        res = {p: eager_steps(r, torch, stream, w, host, f, 4, 12) for p, f in parts.items()}
+        host.close()
+        print(json.dumps({
+            "comparison": f"gather partition, {name} (B={w.B}, K={w.K}, S={w.S}, "
+                          f"{pct}% adjacent reuse)",
+            "effective_GBps": {p: v["gather_GBps"] for p, v in res.items()},
+            "gather_us": {p: v["gather_us"] for p, v in res.items()},
+            "rows_per_step": res["per_row"]["rows_per_step"],
+            "hit_rate": res["per_row"]["hit_rate"],
+            f"per_row_over_{other}": round(res["per_row"]["gather_GBps"] /
+                                           res[other]["gather_GBps"], 2)}), flush=True)
+    w = make("matching")
+    host = r.HostPool(w.host_bytes)
+    w.fill_host_kv(host.array)
+    reuse = eager_steps(r, torch, stream, w, host, 0, 4, 30)
+    offload = eager_steps(r, torch, stream, w, host, r.FLAG_NO_REUSE, 4, 30)
+    host.close()
+    print(json.dumps({
+        "comparison": "recall step with reuse vs KV Offload (no reuse), matching workload",
+        "with_reuse": reuse, "kv_offload": offload,
+        "step_ratio_offload_over_reuse": round(offload["step_us"] / reuse["step_us"], 3)}),
+        flush=True)
+    return 0
+
+
 def contiguous_gather_peak(r, torch, stream, row_bytes=1280, rows=1 << 19, blocks=0):
     """The gather kernel on a miss list of consecutive host rows: the
     zero-copy streaming rate of the same kernel without scattered reads."""
@@ -264,6 +349,8 @@ def main():
         return 2
     if args.probe_sweep:
         return probe_sweep(args)
+    if args.ratios:
+        return ratios(args)
     import torch
     import recall_step_amd as r
     from workloads import make

@@ -68,6 +68,22 @@ extern "C" {
 /* Config flags. */
 #define AVSG_FLAG_SKIP_GATHER 1u   /* avsg_step runs Stage One only (no host
                                       pool needed) */
+/* Comparison points the AVSG page measures against (results are unchanged
+ * by the two partition flags; they exist to time the alternatives). */
+#define AVSG_FLAG_GATHER_BY_REQUEST 2u /* Stage Two gives each request's
+                                      misses to one workgroup (request-level
+                                      core assignment, AVSG s4.3) */
+#define AVSG_FLAG_GATHER_BY_TOPK 4u /* Stage Two splits each token's top-K
+                                      positions into equal ranges, one per
+                                      workgroup, and copies the misses found
+                                      in each (equal top-K partitioning,
+                                      AVSG s4.3); needs topk, hit_mask and
+                                      slot_table in the io */
+#define AVSG_FLAG_NO_REUSE 8u      /* "KV Offload" (AVSG s4.1): no buffer
+                                      reuse; avsg_match makes every valid id a
+                                      miss placed at slot g*K + i (position i
+                                      of query token g), in position order,
+                                      and leaves Q, C, F untouched */
 
 typedef struct avsg_config {
     int32_t B;         /* requests (batch rows), >= 1 */
@@ -194,7 +210,10 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream);
  * avsg_match on this io into its slot of dev_kv, with the missed rows split
  * evenly across workgroups by flat miss index (not by request).  Reads
  * n_miss, the miss list, row_base and host_rows (topk, ctx_len, slot_table
- * and hit_mask may be NULL).  AVSG_EINVAL if host_kv is NULL. */
+ * and hit_mask may be NULL).  With AVSG_FLAG_GATHER_BY_REQUEST or
+ * AVSG_FLAG_GATHER_BY_TOPK the same rows are copied under the other
+ * partition; the by-top-K one reads topk, hit_mask and slot_table instead
+ * of the miss list.  AVSG_EINVAL if host_kv is NULL. */
 int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream);
 
 /* avsg_match followed by avsg_gather (the gather is skipped under

@@ -331,6 +331,70 @@ int orc_step(const orc_cfg* cfg, int32_t* Qall, int32_t* Call, int32_t* Fall,
     return rc;
 }
 
+/*
+ * The "KV Offload" configuration the AVSG page compares against (section
+ * 4.1): the whole KV cache stays in host memory and every selected entry is
+ * transferred at every decode step, with no reuse.  Reading taken: the entry
+ * at position i of query token g of a request lands in that request's slot
+ * g*K + i (a fixed, position-indexed destination; N_q*K <= S).  Every valid
+ * id is a miss; the miss list holds (id, slot) in position order.  Padding
+ * and out-of-range ids are treated as in orc_step.  Q, C and F are not used;
+ * the LOOKUPS and MISSES counters grow by the valid ids, ERRORS as usual.
+ */
+int orc_step_no_reuse(const orc_cfg* cfg, int32_t* CNTall, const int32_t* topk,
+                      const int64_t* row_base, const int32_t* host_rows,
+                      const uint8_t* host_kv, uint8_t* dev_shadow,
+                      int32_t* slot_table, int8_t* hit_mask, int32_t* n_miss,
+                      int32_t* miss_pairs)
+{
+    const int32_t B = cfg->B, Nq = cfg->Nq, K = cfg->K, S = cfg->S;
+    if (B < 0 || Nq < 1 || K < 1 || S < 1 || (int64_t)Nq * K > S) return ORC_EARG;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t* cnt = CNTall + (int64_t)b * 8;
+        const int row_ok = row_base[b] >= 0 && host_rows[b] >= 0 &&
+                           row_base[b] + host_rows[b] <= cfg->host_rows_total;
+        for (int32_t g = 0; g < Nq; ++g) {
+            const int64_t tok = (int64_t)b * Nq + g;
+            const int32_t* X = topk + tok * K;
+            int32_t* O = slot_table + tok * K;
+            int8_t* H = hit_mask + tok * K;
+            int32_t n = 0;
+            for (int32_t i = 0; i < K; ++i) {
+                int32_t x = X[i];
+                if (x == -1) { O[i] = -1; H[i] = -1; continue; }
+                if (!row_ok || x < 0 || x >= host_rows[b]) {
+                    cnt[ORC_ERRORS] |= 1;
+                    O[i] = -1; H[i] = -1; continue;
+                }
+                O[i] = g * K + i;
+                H[i] = 0;
+                if (miss_pairs) {
+                    int32_t* mp = miss_pairs + (tok * K + n) * 2;
+                    mp[0] = x;
+                    mp[1] = g * K + i;
+                }
+                ++n;
+            }
+            n_miss[tok] = n;
+            bump(&cnt[ORC_LOOKUPS], n);
+            bump(&cnt[ORC_MISSES], n);
+        }
+    }
+    if (host_kv && dev_shadow && miss_pairs) {
+        const int64_t rb = cfg->row_bytes;
+        for (int32_t b = 0; b < B; ++b)
+            for (int32_t g = 0; g < Nq; ++g) {
+                const int64_t tok = (int64_t)b * Nq + g;
+                for (int32_t r = 0; r < n_miss[tok]; ++r) {
+                    const int32_t* mp = miss_pairs + (tok * K + r) * 2;
+                    memcpy(dev_shadow + ((int64_t)b * S + mp[1]) * rb,
+                           host_kv + (row_base[b] + mp[0]) * rb, (size_t)rb);
+                }
+            }
+    }
+    return ORC_OK;
+}
+
 /* Empty state: no bucket words, no cached ids, all slots dead, counters 0. */
 void orc_state_reset(const orc_cfg* cfg, int32_t* Q, int32_t* C, int32_t* F,
                      int32_t* CNT)

@@ -40,6 +40,9 @@ CNT_HITS, CNT_LOOKUPS, CNT_MISSES, CNT_LOST_COLLISION, CNT_LOST_EXHAUSTED, \
 ERR_OUT_OF_RANGE = 1
 ERR_DUPLICATE = 2
 FLAG_SKIP_GATHER = 1
+FLAG_GATHER_BY_REQUEST = 2
+FLAG_GATHER_BY_TOPK = 4
+FLAG_NO_REUSE = 8
 
 
 class AvsgConfig(ctypes.Structure):

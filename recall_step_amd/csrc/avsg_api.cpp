@@ -37,10 +37,12 @@ bool match_io_ok(const avsg_step_io* io) {
            (io->miss_pairs == nullptr || aligned16(io->miss_pairs));
 }
 
-// Fields Stage Two reads.
-bool gather_io_ok(const avsg_step_io* io) {
-    return io && io->row_base && io->host_rows && io->n_miss &&
-           (io->miss_pairs == nullptr || aligned16(io->miss_pairs));
+// Fields Stage Two reads (the by-top-K partition reads the top-K ids, hit
+// mask and slot table instead of the miss list).
+bool gather_io_ok(const avsg_step_io* io, uint32_t flags) {
+    if (!io || !io->row_base || !io->host_rows) return false;
+    if (flags & AVSG_FLAG_GATHER_BY_TOPK) return io->topk && io->hit_mask && io->slot_table;
+    return io->n_miss && (io->miss_pairs == nullptr || aligned16(io->miss_pairs));
 }
 
 int check_device(const avsg_handle* h) {
@@ -101,7 +103,11 @@ int avsg_validate_config(const avsg_config* c) {
         return AVSG_EINVAL;
     if (c->stage1_threads != 0 && c->K > c->stage1_threads * avsg::kMaxIdsPerThread)
         return AVSG_EINVAL;
-    if (c->flags & ~AVSG_FLAG_SKIP_GATHER) return AVSG_EINVAL;
+    const uint32_t known = AVSG_FLAG_SKIP_GATHER | AVSG_FLAG_GATHER_BY_REQUEST |
+                           AVSG_FLAG_GATHER_BY_TOPK | AVSG_FLAG_NO_REUSE;
+    if (c->flags & ~known) return AVSG_EINVAL;
+    if ((c->flags & AVSG_FLAG_GATHER_BY_REQUEST) && (c->flags & AVSG_FLAG_GATHER_BY_TOPK))
+        return AVSG_EINVAL;
     return AVSG_OK;
 }
 
@@ -192,6 +198,23 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
     int rc = check_device(h);
     if (rc != AVSG_OK) return rc;
     const avsg_config& c = h->cfg;
+    if (c.flags & AVSG_FLAG_NO_REUSE) {
+        avsg::OffloadArgs o;
+        o.CNT = h->bufs.CNT;
+        o.topk = io->topk;
+        o.row_base = io->row_base;
+        o.host_rows = io->host_rows;
+        o.slot_table = io->slot_table;
+        o.hit_mask = io->hit_mask;
+        o.n_miss = io->n_miss;
+        o.pairs = io->miss_pairs ? io->miss_pairs : h->ws_pairs;
+        o.host_rows_total = h->bufs.host_rows_total;
+        o.B = c.B;
+        o.Nq = c.N_q;
+        o.K = c.K;
+        hipError_t e = avsg::launch_offload(o, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? AVSG_OK : hip_fail(e);
+    }
     avsg::Stage1Args a;
     a.Q = h->bufs.Q;
     a.C = h->bufs.C;
@@ -221,7 +244,7 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
 }
 
 int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream) {
-    if (!h || !gather_io_ok(io)) return AVSG_EINVAL;
+    if (!h || !gather_io_ok(io, h->cfg.flags)) return AVSG_EINVAL;
     if (!h->host_dev) return AVSG_EINVAL;
     int rc = check_device(h);
     if (rc != AVSG_OK) return rc;
@@ -229,6 +252,9 @@ int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream) {
     avsg::GatherArgs a;
     a.n_miss = io->n_miss;
     a.pairs = io->miss_pairs ? io->miss_pairs : h->ws_pairs;
+    a.topk = io->topk;
+    a.hit_mask = io->hit_mask;
+    a.slot_table = io->slot_table;
     a.row_base = io->row_base;
     a.host_rows = io->host_rows;
     a.host = h->host_dev;
@@ -239,6 +265,9 @@ int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream) {
     a.K = c.K;
     a.S = c.S;
     a.row_bytes = c.row_bytes;
+    a.mode = (c.flags & AVSG_FLAG_GATHER_BY_REQUEST) ? avsg::kGatherByRequest
+             : (c.flags & AVSG_FLAG_GATHER_BY_TOPK)  ? avsg::kGatherByTopk
+                                                     : avsg::kGatherByRow;
     hipError_t e = avsg::launch_gather(a, h->gather_blocks, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }

@@ -16,6 +16,12 @@
 // contiguous host bytes per instruction, and each lane keeps several loads in
 // flight before storing.  A grid of twice the CU count measured best on
 // gfx950: the host link is saturated with fewer requests queued.
+//
+// The two partitions the page compares against share the copy loop: by
+// request (workgroup w copies all misses of requests w, w+G, ...) and by
+// top-K position (each token's K positions are cut into equal ranges, one per
+// workgroup, and each range's misses are copied).  Results are identical;
+// only the balance of work across workgroups differs.
 #include "internal.h"
 
 namespace avsg {
@@ -34,6 +40,66 @@ __device__ inline int wave_incl_scan(int v) {
     return v;
 }
 
+// Exclusive scan of one int per thread over a T-thread workgroup.
+__device__ inline int block_excl_scan(int v, int32_t* sWave, int* total) {
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) sWave[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        const int t = lane < T / 64 ? sWave[lane] : 0;
+        const int ti = wave_incl_scan(t);
+        if (lane < T / 64) sWave[lane] = ti - t;
+        if (lane == T / 64 - 1) sWave[T / 64] = ti;
+    }
+    __syncthreads();
+    *total = sWave[T / 64];
+    const int r = incl - v + sWave[w];
+    __syncthreads();
+    return r;
+}
+
+// Byte offsets of one miss (host id x of request bq into slot v), or a
+// negative source for a row that must not be copied.
+__device__ inline void row_offsets(const GatherArgs& a, int bq, int32_t x, int32_t v,
+                                   int64_t* src, int64_t* dst) {
+    const int64_t rb = a.row_base[bq];
+    const int32_t hr = a.host_rows[bq];
+    const bool ok = x >= 0 && x < hr && v >= 0 && v < a.S && rb >= 0 &&
+                    rb + hr <= a.host_rows_total;
+    *src = ok ? (rb + x) * int64_t(a.row_bytes) : int64_t(-1);
+    *dst = (int64_t(bq) * a.S + v) * int64_t(a.row_bytes);
+}
+
+// Copy nrows rows whose byte offsets are in LDS.  The loads of an iteration
+// are unconditional (a rejected row reads row 0 of the pool, always in
+// bounds) so all kUnroll are in flight at once; only the stores are
+// predicated.  Ends with a barrier so the offsets may be rewritten.
+__device__ inline void copy_rows(const GatherArgs& a, const int64_t* sSrc, const int64_t* sDst,
+                                 int nrows) {
+    const int cpr = a.row_bytes >> 4;  // 16-byte chunks per row
+    const int items = nrows * cpr;
+    for (int it0 = threadIdx.x; it0 < items; it0 += T * kUnroll) {
+        int4 v[kUnroll];
+        int64_t d[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int it = it0 + u * T;
+            const int itc = min(it, items - 1);
+            const int row = itc / cpr;
+            const int c = itc - row * cpr;
+            const int64_t src = sSrc[row];
+            v[u] = *reinterpret_cast<const int4*>(a.host + max(src, int64_t(0)) +
+                                                  int64_t(c) * 16);
+            d[u] = (it < items && src >= 0) ? sDst[row] + int64_t(c) * 16 : int64_t(-1);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (d[u] >= 0) *reinterpret_cast<int4*>(a.dev + d[u]) = v[u];
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
     extern __shared__ int32_t sOff[];  // [ntok + 1] exclusive prefix of n
     __shared__ int64_t sSrc[kGatherRowsPerPass];
@@ -44,29 +110,17 @@ __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
     if (a.host_rows_total <= 0) return;
 
     const int tid = threadIdx.x;
-    const int lane = __lane_id();
-    const int w = tid >> 6;
     const int ntok = a.B * a.Nq;
 
     // Exclusive scan of the miss counts, in chunks of T tokens.
     int carry = 0;
     for (int base = 0; base < ntok; base += T) {
         const int k = base + tid;
-        int v = k < ntok ? a.n_miss[k] : 0;
-        v = min(max(v, 0), a.K);
-        const int incl = wave_incl_scan(v);
-        if (lane == 63) sWave[w] = incl;
-        __syncthreads();
-        if (w == 0) {
-            const int t = lane < T / 64 ? sWave[lane] : 0;
-            const int ti = wave_incl_scan(t);
-            if (lane < T / 64) sWave[lane] = ti - t;
-            if (lane == T / 64 - 1) sWave[T / 64] = ti;
-        }
-        __syncthreads();
-        if (k < ntok) sOff[k] = carry + incl - v + sWave[w];
-        carry += sWave[T / 64];
-        __syncthreads();
+        const int v = k < ntok ? min(max(a.n_miss[k], 0), a.K) : 0;
+        int tot;
+        const int off = block_excl_scan(v, sWave, &tot);
+        if (k < ntok) sOff[k] = carry + off;
+        carry += tot;
     }
     if (tid == 0) sOff[ntok] = carry;
     __syncthreads();
@@ -74,7 +128,6 @@ __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
     const int64_t M = carry;
     const int64_t lo = M * blockIdx.x / gridDim.x;
     const int64_t hi = M * (blockIdx.x + 1) / gridDim.x;
-    const int cpr = a.row_bytes >> 4;  // 16-byte chunks per row
 
     for (int64_t base = lo; base < hi; base += kGatherRowsPerPass) {
         const int nrows = int(min<int64_t>(kGatherRowsPerPass, hi - base));
@@ -88,40 +141,67 @@ __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
             }
             const int tok = l;
             const int r = m - sOff[tok];
-            const int bq = tok / a.Nq;
             const int2 pr = reinterpret_cast<const int2*>(a.pairs)[size_t(tok) * a.K + r];
-            const int64_t rb = a.row_base[bq];
-            const int32_t hr = a.host_rows[bq];
-            const bool ok = pr.x >= 0 && pr.x < hr && pr.y >= 0 && pr.y < a.S &&
-                            rb >= 0 && rb + hr <= a.host_rows_total;
-            sSrc[i] = ok ? (rb + pr.x) * int64_t(a.row_bytes) : int64_t(-1);
-            sDst[i] = (int64_t(bq) * a.S + pr.y) * int64_t(a.row_bytes);
+            row_offsets(a, tok / a.Nq, pr.x, pr.y, &sSrc[i], &sDst[i]);
         }
         __syncthreads();
-        // Consecutive lanes move consecutive 16-byte chunks of a row.  The
-        // loads of an iteration are unconditional (a rejected row reads row 0
-        // of the pool, always in bounds) so all kUnroll are in flight at
-        // once; only the stores are predicated.
-        const int items = nrows * cpr;
-        for (int it0 = tid; it0 < items; it0 += T * kUnroll) {
-            int4 v[kUnroll];
-            int64_t d[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int it = it0 + u * T;
-                const int itc = min(it, items - 1);
-                const int row = itc / cpr;
-                const int c = itc - row * cpr;
-                const int64_t src = sSrc[row];
-                v[u] = *reinterpret_cast<const int4*>(a.host + max(src, int64_t(0)) +
-                                                      int64_t(c) * 16);
-                d[u] = (it < items && src >= 0) ? sDst[row] + int64_t(c) * 16 : int64_t(-1);
+        copy_rows(a, sSrc, sDst, nrows);
+    }
+}
+
+// Request-level assignment: workgroup w copies every miss of requests
+// w, w + G, w + 2G, ...
+__global__ __launch_bounds__(T) void gather_by_request_kernel(GatherArgs a) {
+    __shared__ int64_t sSrc[kGatherRowsPerPass];
+    __shared__ int64_t sDst[kGatherRowsPerPass];
+    if (a.host_rows_total <= 0) return;
+    for (int bq = blockIdx.x; bq < a.B; bq += gridDim.x) {
+        for (int g = 0; g < a.Nq; ++g) {
+            const size_t tok = size_t(bq) * a.Nq + g;
+            const int n = min(max(a.n_miss[tok], 0), a.K);
+            for (int base = 0; base < n; base += kGatherRowsPerPass) {
+                const int nrows = min(kGatherRowsPerPass, n - base);
+                for (int i = threadIdx.x; i < nrows; i += T) {
+                    const int2 pr = reinterpret_cast<const int2*>(a.pairs)[tok * a.K + base + i];
+                    row_offsets(a, bq, pr.x, pr.y, &sSrc[i], &sDst[i]);
+                }
+                __syncthreads();
+                copy_rows(a, sSrc, sDst, nrows);
             }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                if (d[u] >= 0) *reinterpret_cast<int4*>(a.dev + d[u]) = v[u];
         }
-        __syncthreads();
+    }
+}
+
+// Equal top-K partitioning: each token's K positions are cut into P ranges
+// of equal length (P chosen so that B * N_q * P covers the grid); unit
+// (token, range) goes to workgroup unit mod G, which copies the misses
+// (hit_mask 0) found in its range from the top-K ids and the slot table.
+__global__ __launch_bounds__(T) void gather_by_topk_kernel(GatherArgs a) {
+    __shared__ int64_t sSrc[kGatherRowsPerPass];
+    __shared__ int64_t sDst[kGatherRowsPerPass];
+    __shared__ int32_t sWave[T / 64 + 1];
+    if (a.host_rows_total <= 0) return;
+    const int ntok = a.B * a.Nq;
+    const int P = max(1, (int(gridDim.x) + ntok - 1) / ntok);
+    const int len = (a.K + P - 1) / P;
+    const int units = ntok * P;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int tok = u / P;
+        const int bq = tok / a.Nq;
+        const int lo = (u - tok * P) * len;
+        const int hi = min(a.K, lo + len);
+        // Positions are taken T at a time (one per thread), misses
+        // compacted into LDS, then copied.
+        for (int base = lo; base < hi; base += T) {
+            const int i = base + threadIdx.x;
+            const size_t e = size_t(tok) * a.K + i;
+            const bool miss = i < hi && a.hit_mask[e] == 0;
+            int tot;
+            const int off = block_excl_scan(miss ? 1 : 0, sWave, &tot);
+            if (miss) row_offsets(a, bq, a.topk[e], a.slot_table[e], &sSrc[off], &sDst[off]);
+            __syncthreads();
+            if (tot > 0) copy_rows(a, sSrc, sDst, tot);
+        }
     }
 }
 
@@ -143,8 +223,14 @@ __global__ __launch_bounds__(256) void state_init_kernel(InitArgs a) {
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s) {
-    const size_t lds = size_t(a.B * a.Nq + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(T), lds, s, a);
+    if (a.mode == kGatherByRequest) {
+        hipLaunchKernelGGL(gather_by_request_kernel, dim3(blocks), dim3(T), 0, s, a);
+    } else if (a.mode == kGatherByTopk) {
+        hipLaunchKernelGGL(gather_by_topk_kernel, dim3(blocks), dim3(T), 0, s, a);
+    } else {
+        const size_t lds = size_t(a.B * a.Nq + 1) * sizeof(int32_t);
+        hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(T), lds, s, a);
+    }
     return hipGetLastError();
 }
 

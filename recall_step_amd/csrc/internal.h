@@ -92,15 +92,33 @@ struct Stage1Args {
     uint32_t a1, a2, afp;
 };
 
+enum GatherMode { kGatherByRow = 0, kGatherByRequest = 1, kGatherByTopk = 2 };
+
 struct GatherArgs {
     const int32_t* __restrict__ n_miss;
     const int32_t* __restrict__ pairs;
+    const int32_t* __restrict__ topk;        // by-top-K mode only
+    const int8_t* __restrict__ hit_mask;     // by-top-K mode only
+    const int32_t* __restrict__ slot_table;  // by-top-K mode only
     const int64_t* __restrict__ row_base;
     const int32_t* __restrict__ host_rows;
     const uint8_t* __restrict__ host;  // device alias of the pinned pool
     uint8_t* __restrict__ dev;
     int64_t host_rows_total;
-    int32_t B, Nq, K, S, row_bytes;
+    int32_t B, Nq, K, S, row_bytes, mode;
+};
+
+struct OffloadArgs {
+    int32_t* __restrict__ CNT;
+    const int32_t* __restrict__ topk;
+    const int64_t* __restrict__ row_base;
+    const int32_t* __restrict__ host_rows;
+    int32_t* __restrict__ slot_table;
+    int8_t* __restrict__ hit_mask;
+    int32_t* __restrict__ n_miss;
+    int32_t* __restrict__ pairs;
+    int64_t host_rows_total;
+    int32_t B, Nq, K;
 };
 
 struct InitArgs {
@@ -117,6 +135,7 @@ int stage1_threads(int K, int requested);
 hipError_t stage1_prepare(size_t lds_bytes);
 hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds_bytes, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s);
+hipError_t launch_offload(const OffloadArgs& a, hipStream_t s);
 hipError_t launch_state_init(const InitArgs& a, hipStream_t s);
 
 }  // namespace avsg

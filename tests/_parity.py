@@ -30,15 +30,17 @@ def make_cfg(r, w, flags=0, gather_blocks=0, stage1_threads=0):
 class Pair:
     """A GPU handle and an oracle on one workload."""
 
-    def __init__(self, w, gather=True, gather_blocks=0, shadow=True, stage1_threads=0):
+    def __init__(self, w, gather=True, gather_blocks=0, shadow=True, stage1_threads=0,
+                 flags=0):
         import torch
         import recall_step_amd as r
         self.r, self.torch, self.w = r, torch, w
         self.gather = gather
+        self.no_reuse = bool(flags & r.FLAG_NO_REUSE)
         self.host = r.HostPool(w.host_bytes) if gather else None
         if gather:
             w.fill_host_kv(self.host.array)
-        flags = 0 if gather else r.FLAG_SKIP_GATHER
+        flags |= 0 if gather else r.FLAG_SKIP_GATHER
         self.rs = r.RecallStep(make_cfg(r, w, flags, gather_blocks, stage1_threads),
                                self.host, w.host_rows_total)
         self.oracle = Oracle.for_workload(
@@ -57,7 +59,8 @@ class Pair:
 
     def oracle_step(self, t):
         w = self.w
-        return self.oracle.step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
+        step = self.oracle.step_no_reuse if self.no_reuse else self.oracle.step
+        return step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
 
     def compare(self, ref, ctx, check_kv=False):
         torch = self.torch
@@ -90,14 +93,15 @@ class Pair:
 
 
 def run_parity(w, steps=None, kv_every=None, gather=True, gather_blocks=0, label=None,
-               stage1_threads=0):
+               stage1_threads=0, flags=0):
     """Step both sides through w, comparing everything after every step;
     returns the oracle's counters, int64 [B][8]."""
     label = label or w.name
     steps = w.steps if steps is None else steps
     say(f"[parity] {label}: B={w.B} Nq={w.Nq} K={w.K} S={w.S} L={w.L} R={w.R} "
         f"row={w.row_bytes} host_rows={w.host_rows_total} steps={steps} gather={gather}")
-    p = Pair(w, gather=gather, gather_blocks=gather_blocks, stage1_threads=stage1_threads)
+    p = Pair(w, gather=gather, gather_blocks=gather_blocks, stage1_threads=stage1_threads,
+             flags=flags)
     try:
         for t in range(steps):
             p.gpu_step(t)

@@ -139,6 +139,45 @@ def test_stage_one_workgroup_size_does_not_change_results(name, threads):
     run_parity(w, gather=False, stage1_threads=threads, label=f"{name} T={threads}")
 
 
+@pytest.mark.parametrize("part", ["request", "topk"])
+@pytest.mark.parametrize("name", ["matching", "mtp3", "imbalanced"])
+def test_gather_partitions_copy_the_same_rows(name, part):
+    """The request-level and equal-top-K partitions the page compares
+    against move the same rows into the same slots as the per-row split."""
+    import recall_step_amd as r
+    flag = r.FLAG_GATHER_BY_REQUEST if part == "request" else r.FLAG_GATHER_BY_TOPK
+    w = make(name, steps=5) if name == "matching" else make(name, steps=5, B=6)
+    run_parity(w, kv_every=1, flags=flag, label=f"{name} by {part}")
+
+
+@pytest.mark.parametrize("gblocks", [0, 3])
+def test_gather_partitions_on_fuzz_corpus(gblocks):
+    """Tiny random cases (padding, out-of-range and speculative ids, MTP)
+    under both comparison partitions, with the default grid and a grid
+    smaller than the batch."""
+    import recall_step_amd as r
+    for seed in range(0, 160, 8):
+        for flag in (r.FLAG_GATHER_BY_REQUEST, r.FLAG_GATHER_BY_TOPK):
+            run_parity(gen_fuzz(seed), kv_every=1, flags=flag, gather_blocks=gblocks)
+
+
+@pytest.mark.parametrize("name", ["tiny", "matching", "mtp3"])
+def test_no_reuse_mode_matches_oracle(name):
+    """"KV Offload": every valid selected row copied to slot g*K + i each
+    step, in position order."""
+    import recall_step_amd as r
+    w = make(name, steps=4) if name != "mtp3" else make(name, steps=4, B=4)
+    run_parity(w, kv_every=1, flags=r.FLAG_NO_REUSE, label=f"{name} no reuse")
+
+
+def test_no_reuse_mode_on_fuzz_corpus():
+    import recall_step_amd as r
+    for seed in range(0, 160, 4):
+        run_parity(gen_fuzz(seed), kv_every=1, flags=r.FLAG_NO_REUSE)
+        run_parity(gen_fuzz(seed), kv_every=1,
+                   flags=r.FLAG_NO_REUSE | r.FLAG_GATHER_BY_TOPK)
+
+
 def test_state_beyond_lds_is_unsupported():
     """K = S = 8192 needs more than 160 KiB of LDS: create refuses it."""
     import recall_step_amd as r

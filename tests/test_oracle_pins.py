@@ -386,3 +386,41 @@ def test_rate_definitions_reproduce_printed_figures():
     assert int(100 * rates.latency_reduction(tp["kv_offload_ms"], tp["avsg_ms"])) == \
         round(100 * tp["reduction"])
     assert rates.adjacent_reuse([1, 2, 3, 4], [3, 4, 5, 6]) == 0.5
+
+
+# --- "KV Offload" comparison point (AVSG page, section 4.1) ---------------
+
+@pytest.mark.parametrize("seed", range(40))
+def test_no_reuse_copies_every_selected_row_every_step(seed):
+    """With no reuse every valid selected id is transferred at every step
+    (section 4.1): copies = valid ids, so the reuse rate 1 - copies / lookups
+    of section 4.4 is 0; slots are distinct within a request, and after the
+    copy each slot holds the host row of the id that maps to it."""
+    w = gen_fuzz(seed)
+    hk = np.random.default_rng([seed, 5]).integers(0, 256, w.host_bytes, dtype=np.uint8)
+    o = Oracle.for_workload(w, host_kv=hk)
+    for t in range(w.steps):
+        before = o.CNT.astype(np.int64).copy()
+        out = o.step_no_reuse(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
+        d = (o.CNT.astype(np.int64) - before).sum(0)
+        valid = 0
+        for b in range(w.B):
+            hr = int(w.host_rows[b])
+            ok_rows = w.row_base[b] + hr <= w.host_rows_total
+            slots = []
+            for g in range(w.Nq):
+                ids = w.topk[t, b, g]
+                ok = (ids >= 0) & (ids < hr) & ok_rows
+                valid += int(ok.sum())
+                assert out.n_miss[b, g] == ok.sum()
+                assert (out.hit_mask[b, g][ok] == 0).all()
+                assert (out.hit_mask[b, g][~ok] == -1).all()
+                assert (out.slot_table[b, g][~ok] == -1).all()
+                slots += out.slot_table[b, g][ok].tolist()
+                for i in np.flatnonzero(ok):
+                    x, v = int(ids[i]), int(out.slot_table[b, g, i])
+                    row = hk[(w.row_base[b] + x) * w.row_bytes:(w.row_base[b] + x + 1) * w.row_bytes]
+                    assert np.array_equal(o.shadow[b, v], row)
+            assert len(slots) == len(set(slots)) and all(0 <= v < w.S for v in slots)
+        assert d[oracle.MISSES] == valid and d[oracle.LOOKUPS] == valid
+        assert d[oracle.HITS] == 0

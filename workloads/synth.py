@@ -327,9 +327,53 @@ def gen_imbalanced(steps=64, B=64):
     return w
 
 
+def gen_reuse(B, reuse, steps=16, name=None, seed=606):
+    """Fixed adjacent-step reuse, for the transfer-partition comparison the
+    AVSG page makes at B = 1 with 25 % reuse and at B = 8 with 75 % reuse
+    (section 4.3): context 65536, K = 2048, S = 4096, 1280-B rows.
+
+    Step 0 draws K distinct ids uniformly; each later step keeps
+    round(reuse * K) of the previous ids (chosen uniformly) and adds fresh
+    distinct ids drawn uniformly from the rest of the context.  Ids are
+    emitted in random order.
+    """
+    ctx, K, S = 65536, 2048, 4096
+    Nq = 1
+    keep = int(round(reuse * K))
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, int(round(reuse * 100)), b])
+        prev = None
+        for t in range(steps):
+            if prev is None:
+                ids = rng.choice(ctx, K, replace=False)
+            else:
+                kept = rng.choice(prev, keep, replace=False)
+                taken = np.zeros(ctx, bool)
+                taken[prev] = True
+                new = _take_distinct(rng, K - keep, _uniform_sampler(rng, ctx), taken)
+                ids = np.concatenate([kept, new])
+            ids = rng.permutation(ids)
+            topk[t, b, 0] = ids
+            prev = ids
+    name = name or f"reuse{int(round(reuse * 100))}_b{B}"
+    return Workload(name, B, Nq, K, S, 1280, steps, seed, topk,
+                    np.full((steps, B), ctx, np.int32), np.full(B, ctx, np.int32),
+                    np.arange(B, dtype=np.int64) * ctx)
+
+
+def gen_reuse25_b1(steps=16):
+    return gen_reuse(1, 0.25, steps)
+
+
+def gen_reuse75_b8(steps=16):
+    return gen_reuse(8, 0.75, steps)
+
+
 GENERATORS = {"tiny": gen_tiny, "matching": gen_matching,
               "residency": gen_residency, "mtp3": gen_mtp3,
-              "imbalanced": gen_imbalanced}
+              "imbalanced": gen_imbalanced, "reuse25_b1": gen_reuse25_b1,
+              "reuse75_b8": gen_reuse75_b8}
 
 
 def make(name: str, **kw) -> Workload:
