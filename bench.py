@@ -277,7 +277,35 @@ def ratios(args):
     w.fill_host_kv(host.array)
     reuse = eager_steps(r, torch, stream, w, host, 0, 4, 30)
     offload = eager_steps(r, torch, stream, w, host, r.FLAG_NO_REUSE, 4, 30)
+    merge = eager_steps(r, torch, stream, w, host, r.FLAG_SORT_MERGE, 4, 30)
     host.close()
+    print(json.dumps({
+        "comparison": "matching latency, hash probe vs sort-merge matcher, matching "
+                      "workload (B=8, K=S=2048)",
+        "hash_stage1_us": reuse["stage1_us"], "sort_merge_stage1_us": merge["stage1_us"],
+        "sort_merge_over_hash": round(merge["stage1_us"] / reuse["stage1_us"], 2),
+        "hash_hit_rate": reuse["hit_rate"], "sort_merge_hit_rate": merge["hit_rate"]}),
+        flush=True)
+    # Matching latency against K at fixed S and against S at fixed K (one
+    # request, 75 % adjacent reuse, Stage One only).
+    from workloads.synth import gen_reuse
+    for label, shapes in (("K x8 at S=2048", [(256, 2048), (2048, 2048)]),
+                          ("S x16 at K=256", [(256, 512), (256, 8192)])):
+        row = {}
+        for K_, S_ in shapes:
+            wk = gen_reuse(1, 0.75, steps=16, K=K_, S=S_)
+            hk = r.HostPool(wk.host_bytes)
+            wk.fill_host_kv(hk.array)
+            row[f"K={K_},S={S_}"] = {
+                "hash": eager_steps(r, torch, stream, wk, hk, 0, 4, 12)["stage1_us"],
+                "sort_merge": eager_steps(r, torch, stream, wk, hk, r.FLAG_SORT_MERGE,
+                                          4, 12)["stage1_us"]}
+            hk.close()
+        a, b_ = (row[k] for k in row)
+        print(json.dumps({"comparison": f"Stage-One latency scaling, {label}", "us": row,
+                          "hash_growth": round(b_["hash"] / a["hash"], 2),
+                          "sort_merge_growth": round(b_["sort_merge"] / a["sort_merge"], 2)}),
+              flush=True)
     print(json.dumps({
         "comparison": "recall step with reuse vs KV Offload (no reuse), matching workload",
         "with_reuse": reuse, "kv_offload": offload,

@@ -84,6 +84,17 @@ extern "C" {
                                       miss placed at slot g*K + i (position i
                                       of query token g), in position order,
                                       and leaves Q, C, F untouched */
+#define AVSG_FLAG_SORT_MERGE 16u   /* the sort-merge matcher the page
+                                      compares against (GatherSelection
+                                      style, AVSG s2 and s4.2): a valid id
+                                      cached in some row is a hit and keeps
+                                      that row (the lowest); rows not yet
+                                      referenced in the step are free and the
+                                      misses in ascending (id, position) take
+                                      them in ascending order; no lifetimes,
+                                      no hash table; C as the cached ids, Q
+                                      and F untouched; end-of-step
+                                      invalidation as usual */
 
 typedef struct avsg_config {
     int32_t B;         /* requests (batch rows), >= 1 */
@@ -176,8 +187,10 @@ int avsg_validate_config(const avsg_config* cfg);
 
 /* LDS bytes the Stage-One kernel needs for cfg (one workgroup holds one
  * request's bucket words, ids and lifetimes, 9 bytes per slot, plus per-token
- * work space), or 0 if cfg does not fit in 160 KiB (gfx950's per-workgroup
- * LDS); avsg_create then returns AVSG_EUNSUPPORTED.  Needs no GPU. */
+ * work space; with AVSG_FLAG_SORT_MERGE the sort-merge matcher's cached ids
+ * and sort keys), or 0 if cfg does not fit in 160 KiB (gfx950's
+ * per-workgroup LDS); avsg_create then returns AVSG_EUNSUPPORTED.  Needs no
+ * GPU. */
 size_t avsg_stage1_lds_bytes(const avsg_config* cfg);
 
 /* Device bytes avsg_create allocates for its workspace.  Needs no GPU. */

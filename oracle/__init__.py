@@ -56,6 +56,8 @@ def _load():
         lib.orc_step.restype = ctypes.c_int
         lib.orc_step_no_reuse.argtypes = [p] * 11
         lib.orc_step_no_reuse.restype = ctypes.c_int
+        lib.orc_step_sort_merge.argtypes = [p] * 13
+        lib.orc_step_sort_merge.restype = ctypes.c_int
         lib.orc_state_reset.argtypes = [p] * 5
         lib.orc_state_reset.restype = None
         lib.orc_version.restype = ctypes.c_int
@@ -158,6 +160,29 @@ class Oracle:
                                        _ptr(self.shadow), _ptr(out.slot_table),
                                        _ptr(out.hit_mask), _ptr(out.n_miss),
                                        _ptr(out.miss_pairs))
+        if rc != 0:
+            raise OracleError(f"oracle step failed: {RC_NAMES.get(rc, rc)}")
+        return out
+
+    def step_sort_merge(self, topk, ctx_len, row_base, host_rows) -> StepOut:
+        """The sort-merge matcher the page compares against (GatherSelection
+        style exact reuse, no lifetimes): see orc_step_sort_merge.  Uses C
+        and CNT; Q and F stay as they are."""
+        B, Nq, K = self.B, self.Nq, self.K
+        topk = np.ascontiguousarray(topk, np.int32).reshape(B, Nq, K)
+        ctx_len = np.ascontiguousarray(ctx_len, np.int32).reshape(B)
+        row_base = np.ascontiguousarray(row_base, np.int64).reshape(B)
+        host_rows = np.ascontiguousarray(host_rows, np.int32).reshape(B)
+        out = StepOut(np.empty((B, Nq, K), np.int32), np.empty((B, Nq, K), np.int8),
+                      np.empty((B, Nq), np.int32), np.zeros((B, Nq, K, 2), np.int32))
+        hk = self.host_kv
+        rc = _load().orc_step_sort_merge(ctypes.byref(self.cfg), _ptr(self.C), _ptr(self.CNT),
+                                         _ptr(topk), _ptr(ctx_len), _ptr(row_base),
+                                         _ptr(host_rows),
+                                         _ptr(hk) if self.shadow is not None else None,
+                                         _ptr(self.shadow), _ptr(out.slot_table),
+                                         _ptr(out.hit_mask), _ptr(out.n_miss),
+                                         _ptr(out.miss_pairs))
         if rc != 0:
             raise OracleError(f"oracle step failed: {RC_NAMES.get(rc, rc)}")
         return out

@@ -395,6 +395,108 @@ int orc_step_no_reuse(const orc_cfg* cfg, int32_t* CNTall, const int32_t* topk,
     return ORC_OK;
 }
 
+/*
+ * The sort-merge matcher the AVSG page compares its hash matching against
+ * (GatherSelection, section 2; the scalar dual-pointer baseline of section
+ * 4.2): exact reuse of cached token ids with no lifetimes and no hash table.
+ * Readings taken, per request and query token in order, on the cached ids C:
+ *   - a valid id x is a hit iff some row caches it; the hit keeps its row
+ *     (the lowest such row);
+ *   - rows not referenced by this step's tokens so far are free; the
+ *     token's misses in ascending (id, position) order take the free rows in
+ *     ascending order, which now cache them;
+ *   - at the end of the step every row caching an id >= N is emptied, as in
+ *     orc_step.
+ * Padding and out-of-range ids are treated as in orc_step.  Q and F are not
+ * used.  Counters: HITS, LOOKUPS, MISSES, LIVE_EVICTIONS, ERRORS.
+ */
+int orc_step_sort_merge(const orc_cfg* cfg, int32_t* Call, int32_t* CNTall,
+                        const int32_t* topk, const int32_t* ctx_len,
+                        const int64_t* row_base, const int32_t* host_rows,
+                        const uint8_t* host_kv, uint8_t* dev_shadow,
+                        int32_t* slot_table, int8_t* hit_mask, int32_t* n_miss,
+                        int32_t* miss_pairs)
+{
+    const int32_t B = cfg->B, Nq = cfg->Nq, K = cfg->K, S = cfg->S;
+    if (B < 0 || Nq < 1 || K < 1 || S < 1 || (int64_t)Nq * K > S) return ORC_EARG;
+    orc_miss* misses = (orc_miss*)malloc(sizeof(orc_miss) * (size_t)K);
+    uint8_t* referenced = (uint8_t*)malloc((size_t)S);
+    if (!misses || !referenced) { free(misses); free(referenced); return ORC_ENOMEM; }
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t* C = Call + (int64_t)b * S;
+        int32_t* cnt = CNTall + (int64_t)b * 8;
+        const int row_ok = row_base[b] >= 0 && host_rows[b] >= 0 &&
+                           row_base[b] + host_rows[b] <= cfg->host_rows_total;
+        memset(referenced, 0, (size_t)S);
+        for (int32_t g = 0; g < Nq; ++g) {
+            const int64_t tok = (int64_t)b * Nq + g;
+            const int32_t* X = topk + tok * K;
+            int32_t* O = slot_table + tok * K;
+            int8_t* H = hit_mask + tok * K;
+            int32_t n_valid = 0, n_hit = 0, n_g = 0, live = 0;
+            /* Hits against the rows as they stand before this token's
+             * installs. */
+            for (int32_t i = 0; i < K; ++i) {
+                int32_t x = X[i];
+                O[i] = -1; H[i] = -1;
+                if (x == -1) continue;
+                if (!row_ok || x < 0 || x >= host_rows[b]) { cnt[ORC_ERRORS] |= 1; continue; }
+                ++n_valid;
+                int32_t row = -1;
+                for (int32_t j = 0; j < S; ++j)
+                    if (C[j] == x) { row = j; break; }
+                if (row >= 0) {
+                    O[i] = row; H[i] = 1; ++n_hit;
+                } else {
+                    misses[n_g].id = x; misses[n_g].pos = i; ++n_g;
+                }
+            }
+            for (int32_t i = 0; i < K; ++i)
+                if (H[i] == 1) referenced[O[i]] = 1;
+            qsort(misses, (size_t)n_g, sizeof(orc_miss), cmp_miss);
+            for (int32_t r = 1; r < n_g; ++r)
+                if (misses[r].id == misses[r - 1].id) cnt[ORC_ERRORS] |= 2;
+            int32_t j = 0;
+            for (int32_t r = 0; r < n_g; ++r) {
+                while (j < S && referenced[j]) ++j;
+                if (j >= S) { free(misses); free(referenced); return ORC_EREVICT; }
+                if (C[j] >= 0) ++live;
+                C[j] = misses[r].id;
+                referenced[j] = 1;
+                O[misses[r].pos] = j;
+                H[misses[r].pos] = 0;
+                if (miss_pairs) {
+                    int32_t* mp = miss_pairs + (tok * K + r) * 2;
+                    mp[0] = misses[r].id;
+                    mp[1] = j;
+                }
+            }
+            n_miss[tok] = n_g;
+            bump(&cnt[ORC_HITS], n_hit);
+            bump(&cnt[ORC_LOOKUPS], n_valid);
+            bump(&cnt[ORC_MISSES], n_g);
+            bump(&cnt[ORC_LIVE_EVICTIONS], live);
+        }
+        for (int32_t j = 0; j < S; ++j)
+            if (C[j] >= ctx_len[b]) C[j] = -1;
+    }
+    free(misses);
+    free(referenced);
+    if (host_kv && dev_shadow && miss_pairs) {
+        const int64_t rb = cfg->row_bytes;
+        for (int32_t b = 0; b < B; ++b)
+            for (int32_t g = 0; g < Nq; ++g) {
+                const int64_t tok = (int64_t)b * Nq + g;
+                for (int32_t r = 0; r < n_miss[tok]; ++r) {
+                    const int32_t* mp = miss_pairs + (tok * K + r) * 2;
+                    memcpy(dev_shadow + ((int64_t)b * S + mp[1]) * rb,
+                           host_kv + (row_base[b] + mp[0]) * rb, (size_t)rb);
+                }
+            }
+    }
+    return ORC_OK;
+}
+
 /* Empty state: no bucket words, no cached ids, all slots dead, counters 0. */
 void orc_state_reset(const orc_cfg* cfg, int32_t* Q, int32_t* C, int32_t* F,
                      int32_t* CNT)

@@ -43,6 +43,7 @@ FLAG_SKIP_GATHER = 1
 FLAG_GATHER_BY_REQUEST = 2
 FLAG_GATHER_BY_TOPK = 4
 FLAG_NO_REUSE = 8
+FLAG_SORT_MERGE = 16
 
 
 class AvsgConfig(ctypes.Structure):

@@ -104,8 +104,11 @@ int avsg_validate_config(const avsg_config* c) {
     if (c->stage1_threads != 0 && c->K > c->stage1_threads * avsg::kMaxIdsPerThread)
         return AVSG_EINVAL;
     const uint32_t known = AVSG_FLAG_SKIP_GATHER | AVSG_FLAG_GATHER_BY_REQUEST |
-                           AVSG_FLAG_GATHER_BY_TOPK | AVSG_FLAG_NO_REUSE;
+                           AVSG_FLAG_GATHER_BY_TOPK | AVSG_FLAG_NO_REUSE |
+                           AVSG_FLAG_SORT_MERGE;
     if (c->flags & ~known) return AVSG_EINVAL;
+    if ((c->flags & AVSG_FLAG_NO_REUSE) && (c->flags & AVSG_FLAG_SORT_MERGE))
+        return AVSG_EINVAL;
     if ((c->flags & AVSG_FLAG_GATHER_BY_REQUEST) && (c->flags & AVSG_FLAG_GATHER_BY_TOPK))
         return AVSG_EINVAL;
     return AVSG_OK;
@@ -113,6 +116,7 @@ int avsg_validate_config(const avsg_config* c) {
 
 size_t avsg_stage1_lds_bytes(const avsg_config* c) {
     if (!c) return 0;
+    if (c->flags & AVSG_FLAG_SORT_MERGE) return avsg::sort_merge_layout(c->S, c->K).total;
     return avsg::stage1_layout(c->S, c->K, c->L).total;
 }
 
@@ -144,7 +148,8 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** 
     if (e != hipSuccess) return hip_fail(e);
     const size_t lds = avsg_stage1_lds_bytes(cfg);
     if (lds == 0 || lds > size_t(prop.sharedMemPerBlock)) return AVSG_EUNSUPPORTED;
-    e = avsg::stage1_prepare(lds);
+    e = (cfg->flags & AVSG_FLAG_SORT_MERGE) ? avsg::sort_merge_prepare(lds)
+                                            : avsg::stage1_prepare(lds);
     if (e != hipSuccess) return hip_fail(e);
 
     const uint8_t* host_dev = nullptr;
@@ -238,8 +243,10 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
     a.a1 = c.a1;
     a.a2 = c.a2;
     a.afp = c.a_fp;
-    hipError_t e = avsg::launch_stage1(a, h->stage1_threads, h->lds_bytes,
-                                       static_cast<hipStream_t>(stream));
+    hipError_t e = (c.flags & AVSG_FLAG_SORT_MERGE)
+                       ? avsg::launch_sort_merge(a, h->lds_bytes, static_cast<hipStream_t>(stream))
+                       : avsg::launch_stage1(a, h->stage1_threads, h->lds_bytes,
+                                             static_cast<hipStream_t>(stream));
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }
 

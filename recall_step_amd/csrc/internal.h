@@ -74,6 +74,36 @@ __host__ __device__ inline Stage1Layout stage1_layout(int S, int K, int L) {
     return o;
 }
 
+// Sort-merge comparison matcher: one 1024-thread workgroup per request.
+constexpr int kSortMergeThreads = 1024;
+
+// LDS layout of the sort-merge workgroup, in bytes from the base.
+//   c     int32  [S]              cached ids
+//   ref   uint8  [S]              row referenced in this step
+//   ckey  uint64 [next_pow2(S)]   sorted (id << 16 | row) keys of the cache
+//   xkey  uint64 [next_pow2(K)]   sorted (id << 16 | position) keys
+//   flag  int8   [K]              miss flag per sorted id
+//   free  int32  [K]              free rows, ascending
+//   scr   int32  [64]             scan scratch and counters
+// total is 0 when the layout does not fit the LDS budget.
+struct SortMergeLayout {
+    size_t c, ref, ckey, xkey, flag, free, scr, total;
+};
+
+__host__ __device__ inline SortMergeLayout sort_merge_layout(int S, int K) {
+    SortMergeLayout o;
+    o.c = 0;
+    o.ref = size_t(S) * 4;
+    o.ckey = round16(o.ref + size_t(S));
+    o.xkey = o.ckey + size_t(next_pow2(S)) * 8;
+    o.flag = o.xkey + size_t(next_pow2(K)) * 8;
+    o.free = round16(o.flag + size_t(K));
+    o.scr = round16(o.free + size_t(K) * 4);
+    o.total = o.scr + 64 * 4;
+    if (o.total > kStage1LdsBudget) o.total = 0;
+    return o;
+}
+
 struct Stage1Args {
     int32_t* __restrict__ Q;
     int32_t* __restrict__ C;
@@ -136,6 +166,8 @@ hipError_t stage1_prepare(size_t lds_bytes);
 hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds_bytes, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s);
 hipError_t launch_offload(const OffloadArgs& a, hipStream_t s);
+hipError_t sort_merge_prepare(size_t lds_bytes);
+hipError_t launch_sort_merge(const Stage1Args& a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_state_init(const InitArgs& a, hipStream_t s);
 
 }  // namespace avsg

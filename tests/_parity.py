@@ -37,6 +37,7 @@ class Pair:
         self.r, self.torch, self.w = r, torch, w
         self.gather = gather
         self.no_reuse = bool(flags & r.FLAG_NO_REUSE)
+        self.sort_merge = bool(flags & r.FLAG_SORT_MERGE)
         self.host = r.HostPool(w.host_bytes) if gather else None
         if gather:
             w.fill_host_kv(self.host.array)
@@ -59,7 +60,8 @@ class Pair:
 
     def oracle_step(self, t):
         w = self.w
-        step = self.oracle.step_no_reuse if self.no_reuse else self.oracle.step
+        step = (self.oracle.step_no_reuse if self.no_reuse else
+                self.oracle.step_sort_merge if self.sort_merge else self.oracle.step)
         return step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
 
     def compare(self, ref, ctx, check_kv=False):

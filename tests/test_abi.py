@@ -45,7 +45,7 @@ def test_config_default_values():
 @pytest.mark.parametrize("field,value", [
     ("S", 3000), ("S", 8), ("S", 131072), ("K", 0), ("K", 4096), ("B", 0),
     ("N_q", 0), ("L", 0), ("L", 128), ("R", -1), ("a1", 2), ("a2", 4),
-    ("a_fp", 0), ("row_bytes", 1000), ("row_bytes", 0), ("flags", 16), ("flags", 6),
+    ("a_fp", 0), ("row_bytes", 1000), ("row_bytes", 0), ("flags", 32), ("flags", 6), ("flags", 24),
     ("gather_blocks", -1), ("stage1_threads", 128), ("stage1_threads", 300),
     ("stage1_threads", 2048)])
 def test_invalid_configs_rejected(field, value):

@@ -178,6 +178,35 @@ def test_no_reuse_mode_on_fuzz_corpus():
                    flags=r.FLAG_NO_REUSE | r.FLAG_GATHER_BY_TOPK)
 
 
+def test_sort_merge_matcher_on_fuzz_corpus():
+    """The sort-merge comparison matcher against its oracle on tiny random
+    cases (padding, out-of-range and speculative ids, MTP)."""
+    import recall_step_amd as r
+    for seed in range(0, 160, 4):
+        run_parity(gen_fuzz(seed), kv_every=1, flags=r.FLAG_SORT_MERGE)
+
+
+@pytest.mark.parametrize("name", ["matching", "reuse75_b8", "mtp3", "tiny"])
+def test_sort_merge_matcher_on_workloads(name):
+    import recall_step_amd as r
+    w = make(name, steps=6) if name != "mtp3" else make(name, steps=4, B=4)
+    cnt = run_parity(w, kv_every=2, flags=r.FLAG_SORT_MERGE, label=f"{name} sort-merge").sum(0)
+    assert cnt[0] > 0
+
+
+def test_sort_merge_repeated_missing_ids():
+    import recall_step_amd as r
+
+    def draw(rng, t, b):
+        ids = rng.choice(50000, 700, replace=False)
+        dup = rng.choice(ids, 20, replace=False)
+        return rng.permutation(np.concatenate([ids, dup])).astype(np.int32)
+
+    w = _stage_one_only("repeated ids", 720, 2048, 5, 2, 50000, draw)
+    cnt = run_parity(w, gather=False, flags=r.FLAG_SORT_MERGE)
+    assert (cnt[:, 6] & 2).all()
+
+
 def test_state_beyond_lds_is_unsupported():
     """K = S = 8192 needs more than 160 KiB of LDS: create refuses it."""
     import recall_step_amd as r

@@ -424,3 +424,66 @@ def test_no_reuse_copies_every_selected_row_every_step(seed):
             assert len(slots) == len(set(slots)) and all(0 <= v < w.S for v in slots)
         assert d[oracle.MISSES] == valid and d[oracle.LOOKUPS] == valid
         assert d[oracle.HITS] == 0
+
+
+# --- sort-merge matcher comparison point (AVSG page, sections 2 and 4.2) ---
+
+def _sort_merge_run(w, hk=None):
+    o = Oracle.for_workload(w, host_kv=hk)
+    outs, before = [], []
+    for t in range(w.steps):
+        before.append(o.C.copy())
+        outs.append(o.step_sort_merge(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows))
+    return o, outs, before
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_sort_merge_hits_are_the_set_intersection(seed):
+    """Recall = selected minus resident (PulseInfer page, recall stage): for
+    a single query token the hits are exactly the valid ids cached before the
+    step, hits keep their row, the misses take increasing rows in increasing
+    id order, and after the copy every slot holds its id's host row."""
+    w = gen_fuzz(seed)
+    w.Nq = 1
+    w.topk = w.topk[:, :, :1, :].copy()
+    hk = np.random.default_rng([seed, 7]).integers(0, 256, w.host_bytes, dtype=np.uint8)
+    o, outs, before = _sort_merge_run(w, hk)
+    for t, out in enumerate(outs):
+        for b in range(w.B):
+            hr = int(w.host_rows[b])
+            ids = w.topk[t, b, 0]
+            ok = (ids >= 0) & (ids < hr)
+            cached = before[t][b]
+            hit = ok & np.isin(ids, cached[cached >= 0])
+            assert np.array_equal(out.hit_mask[b, 0] == 1, hit)
+            assert np.array_equal(out.hit_mask[b, 0] == 0, ok & ~hit)
+            for i in np.flatnonzero(hit):
+                assert cached[out.slot_table[b, 0, i]] == ids[i]
+            miss_i = np.flatnonzero(ok & ~hit)
+            order = miss_i[np.lexsort((miss_i, ids[miss_i]))]
+            assert (np.diff(out.slot_table[b, 0, order]) > 0).all()
+            assert out.n_miss[b, 0] == miss_i.size
+    t = w.steps - 1
+    for b in range(w.B):
+        ids = w.topk[t, b, 0]
+        for i in np.flatnonzero(outs[t].hit_mask[b, 0] >= 0):
+            x, v = int(ids[i]), int(outs[t].slot_table[b, 0, i])
+            if x >= w.ctx_len[t, b]:
+                continue
+            lo = (w.row_base[b] + x) * w.row_bytes
+            assert np.array_equal(o.shadow[b, v], hk[lo:lo + w.row_bytes])
+
+
+def test_sort_merge_with_s_equal_k_tracks_adjacent_step_reuse():
+    """S = K and full, distinct selections: the buffer ends every step holding
+    exactly that step's ids, so the hit rate of step t is the adjacent-step
+    reuse |X_t & X_{t-1}| / K (section 4.4's definition) exactly."""
+    w = make("reuse75_b8", steps=6)
+    w.S = w.K
+    o, outs, before = _sort_merge_run(w)
+    for t in range(1, w.steps):
+        for b in range(w.B):
+            x = w.topk[t, b, 0]
+            hits = int((outs[t].hit_mask[b, 0] == 1).sum())
+            assert hits == np.intersect1d(x, w.topk[t - 1, b, 0]).size
+            assert set(before[t][b].tolist()) == set(w.topk[t - 1, b, 0].tolist())

@@ -327,17 +327,18 @@ def gen_imbalanced(steps=64, B=64):
     return w
 
 
-def gen_reuse(B, reuse, steps=16, name=None, seed=606):
+def gen_reuse(B, reuse, steps=16, name=None, seed=606, K=2048, S=4096):
     """Fixed adjacent-step reuse, for the transfer-partition comparison the
     AVSG page makes at B = 1 with 25 % reuse and at B = 8 with 75 % reuse
-    (section 4.3): context 65536, K = 2048, S = 4096, 1280-B rows.
+    (section 4.3), and for matching latency against K and S (section 4.2):
+    context 65536, K = 2048 and S = 4096 unless given, 1280-B rows.
 
     Step 0 draws K distinct ids uniformly; each later step keeps
     round(reuse * K) of the previous ids (chosen uniformly) and adds fresh
     distinct ids drawn uniformly from the rest of the context.  Ids are
     emitted in random order.
     """
-    ctx, K, S = 65536, 2048, 4096
+    ctx = 65536
     Nq = 1
     keep = int(round(reuse * K))
     topk = np.full((steps, B, Nq, K), -1, np.int32)
