@@ -96,6 +96,15 @@ def parse():
                          "pages measure against (gather partitions at B=1/25%% and "
                          "B=8/75%% reuse; no-reuse KV Offload on the matching "
                          "workload), one JSON line each")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="instead of the step benchmark: N layers of the matching "
+                         "workload, each with its own cache, stepped (a) layer by "
+                         "layer, (b) as one batched launch per stage, (c) with layer "
+                         "l+1's matching overlapping layer l's gather on a second stream")
+    ap.add_argument("--transfer-sweep", action="store_true",
+                    help="instead of the step benchmark: effective host-to-HBM "
+                         "bandwidth against row size, zero-copy gather vs one "
+                         "hipMemcpyAsync per row vs one bulk copy")
     ap.add_argument("--probe-sweep", action="store_true",
                     help="instead of the step benchmark: Stage-One throughput on the "
                          "residency request shape (K=2048, S=8192) at B = 32..512, "
@@ -314,6 +323,153 @@ def ratios(args):
     return 0
 
 
+def layers_mode(args):
+    """N layers of the matching workload through three schedules; all three
+    compute the same results (the tests check it), only the overlap differs."""
+    import torch
+    import recall_step_amd as r
+    from workloads.synth import gen_matching, stack_layers
+
+    torch.cuda.set_device(0)
+    L, warm, steps = args.layers, 4, 20
+    ws = [gen_matching(steps=warm + steps, layer=l) for l in range(L)]
+    st = stack_layers(ws)
+    B = ws[0].B
+    log(f"[bench] {L} layers x B={B}: host pool {st.host_bytes / 1e9:.2f} GB")
+    host = r.HostPool(st.host_bytes)
+    st.fill_host_kv(host.array)
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    topk = torch.from_numpy(np.ascontiguousarray(st.topk)).cuda()
+    ctx = torch.from_numpy(np.ascontiguousarray(st.ctx_len)).cuda()
+    row_base = torch.from_numpy(st.row_base).cuda()
+    host_rows = torch.from_numpy(st.host_rows).cuda()
+
+    def handle(Bn):
+        cfg = r.avsg_config_default(Bn, st.Nq, st.K, st.S, st.row_bytes, L=st.L, R=st.R,
+                                    a1=st.a1, a2=st.a2, a_fp=st.afp)
+        return r.RecallStep(cfg, host, st.host_rows_total, stream=sA)
+
+    per = [handle(B) for _ in range(L)]
+    big = handle(B * L)
+    torch.cuda.synchronize()
+    sl = [slice(l * B, (l + 1) * B) for l in range(L)]
+    ios_per = [[per[l].io(topk[t][sl[l]], ctx[t][sl[l]], row_base[sl[l]], host_rows[sl[l]])
+                for t in range(warm + steps)] for l in range(L)]
+    ios_big = [big.io(topk[t], ctx[t], row_base, host_rows) for t in range(warm + steps)]
+
+    def run(kind):
+        for h in per + [big]:
+            h.state_init(stream=sA)
+        torch.cuda.synchronize()
+        ev = []
+        for t in range(warm + steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(sA)
+            if kind == "batched":
+                r.avsg_step(big.handle, ios_big[t], sA.cuda_stream)
+            elif kind == "sequential":
+                for l in range(L):
+                    r.avsg_step(per[l].handle, ios_per[l][t], sA.cuda_stream)
+            else:
+                sB.wait_stream(sA)
+                for l in range(L):
+                    r.avsg_match(per[l].handle, ios_per[l][t], sA.cuda_stream)
+                    done = torch.cuda.Event()
+                    done.record(sA)
+                    sB.wait_event(done)
+                    r.avsg_gather(per[l].handle, ios_per[l][t], sB.cuda_stream)
+                sA.wait_stream(sB)
+            e1.record(sA)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev[warm:]) * 1e3 / steps
+
+    res = {k: round(run(k), 1) for k in ("sequential", "batched", "pipelined")}
+    for h in per + [big]:
+        h.close()
+    host.close()
+    print(json.dumps({"layers": L, "B_per_layer": B, "workload": "matching per layer",
+                      "step_us": res,
+                      "batched_over_sequential": round(res["batched"] / res["sequential"], 3),
+                      "pipelined_over_sequential": round(res["pipelined"] / res["sequential"],
+                                                         3)}), flush=True)
+    return 0
+
+
+def transfer_sweep(args):
+    """Effective host-to-HBM bandwidth against the size of one row: the
+    zero-copy gather over scattered rows of a 4 GiB pinned pool, one
+    hipMemcpyAsync per row for the same rows, and one bulk copy of the same
+    total (64 MiB per point)."""
+    import torch
+    import recall_step_amd as r
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    hip = hip_runtime()
+    pool_bytes = 4 << 30
+    pool = r.HostPool(pool_bytes)
+    total = 64 << 20
+    rng = np.random.default_rng(77)
+    for row in (256, 512, 1024, 1280, 2048, 4096, 8192, 16384, 65536):
+        M = total // row
+        K, S = (4096, 8192) if M >= 4096 else (M, max(16, 1 << (M - 1).bit_length()))
+        Bn = (M + K - 1) // K
+        pool_rows = pool_bytes // row
+        ids = rng.choice(pool_rows, M, replace=False).astype(np.int32)
+        cfg = r.avsg_config_default(Bn, 1, K, S, row)
+        rs = r.RecallStep(cfg, pool, pool_rows, stream=stream)
+        pairs = np.zeros((Bn, 1, K, 2), np.int32)
+        n = np.zeros((Bn, 1), np.int32)
+        for b in range(Bn):
+            chunk = np.sort(ids[b * K:(b + 1) * K])
+            n[b, 0] = chunk.size
+            pairs[b, 0, :chunk.size, 0] = chunk
+            pairs[b, 0, :chunk.size, 1] = np.arange(chunk.size)
+        tp = torch.from_numpy(pairs).cuda()
+        tn = torch.from_numpy(n).cuda()
+        rb = torch.zeros(Bn, dtype=torch.int64, device="cuda")
+        hr = torch.full((Bn,), pool_rows, dtype=torch.int32, device="cuda")
+        io = r.AvsgStepIO(0, 0, rb.data_ptr(), hr.data_ptr(), rs.slot_table.data_ptr(),
+                          rs.hit_mask.data_ptr(), tn.data_ptr(), tp.data_ptr())
+        best = 1e9
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            r.avsg_gather(rs.handle, io, sh)
+            e1.record(stream)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        zero_copy = M * row / (best * 1e-3) / 1e9
+        # one DMA copy per row (at most 4096 rows timed)
+        m2 = min(M, 4096)
+        dst = rs.dev_kv.data_ptr()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(m2):
+            rc = hip.hipMemcpyAsync(dst + i * row, pool.ptr + int(ids[i]) * row, row, 1, sh)
+            assert rc == 0, rc
+        e1.record(stream)
+        e1.synchronize()
+        per_row = m2 * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = hip.hipMemcpyAsync(dst, pool.ptr, M * row, 1, sh)
+        assert rc == 0, rc
+        e1.record(stream)
+        e1.synchronize()
+        bulk = M * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        rs.close()
+        print(json.dumps({"transfer_sweep": "scattered rows of a 4 GiB pinned pool, 64 MiB per point",
+                          "row_bytes": row, "rows": M,
+                          "zero_copy_gather_GBps": round(zero_copy, 2),
+                          "memcpy_per_row_GBps": round(per_row, 2),
+                          "bulk_memcpy_GBps": round(bulk, 2)}), flush=True)
+    pool.close()
+    return 0
+
+
 def contiguous_gather_peak(r, torch, stream, row_bytes=1280, rows=1 << 19, blocks=0):
     """The gather kernel on a miss list of consecutive host rows: the
     zero-copy streaming rate of the same kernel without scattered reads."""
@@ -379,6 +535,10 @@ def main():
         return probe_sweep(args)
     if args.ratios:
         return ratios(args)
+    if args.layers:
+        return layers_mode(args)
+    if args.transfer_sweep:
+        return transfer_sweep(args)
     import torch
     import recall_step_amd as r
     from workloads import make

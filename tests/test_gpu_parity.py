@@ -207,6 +207,42 @@ def test_sort_merge_repeated_missing_ids():
     assert (cnt[:, 6] & 2).all()
 
 
+def test_layers_batched_equals_per_layer_and_oracle():
+    """Two layers of the matching workload, each with its own cache: one
+    batched launch per stage over the (layer, request) pairs gives the same
+    outputs, state and slot buffer as one handle per layer, and both equal
+    the oracle."""
+    import torch
+    import recall_step_amd as r
+    from workloads.synth import gen_matching, stack_layers
+    say("[parity] 2 layers, batched vs per layer")
+    ws = [gen_matching(steps=4, layer=l) for l in range(2)]
+    st = stack_layers(ws)
+    cnt = run_parity(st, kv_every=1, label="matching x2 stacked").sum(0)
+    assert cnt[1] == 4 * 16 * 2048
+    p = Pair(st)
+    try:
+        B = ws[0].B
+        per = []
+        for l in range(2):
+            cfg = r.avsg_config_default(B, st.Nq, st.K, st.S, st.row_bytes)
+            per.append(r.RecallStep(cfg, p.host, st.host_rows_total))
+        for t in range(st.steps):
+            p.gpu_step(t)
+            for l in range(2):
+                sl = slice(l * B, (l + 1) * B)
+                per[l].step(per[l].io(p.topk[t][sl], p.ctx[t][sl], p.row_base[sl],
+                                      p.host_rows[sl]))
+            torch.cuda.synchronize()
+            for name in ("slot_table", "hit_mask", "n_miss", "Q", "C", "F", "CNT", "dev_kv"):
+                both = torch.cat([getattr(per[l], name) for l in range(2)])
+                assert torch.equal(both, getattr(p.rs, name)), f"step {t}: {name}"
+        for h in per:
+            h.close()
+    finally:
+        p.close()
+
+
 def test_state_beyond_lds_is_unsupported():
     """K = S = 8192 needs more than 160 KiB of LDS: create refuses it."""
     import recall_step_amd as r

@@ -190,20 +190,21 @@ def _window_plus_zipf(rng, perm, ctx, K, win):
     return window, z
 
 
-def gen_matching(steps=64):
+def gen_matching(steps=64, layer=0):
     """Batch 8, context 65536, K=2048, S=2048, 1280-B rows (576 bf16 + 128 fp8).
 
     Every step selects the 256-token recency window [ctx-256, ctx) plus 1792
     distinct ids whose Zipf(s=1.1) ranks are mapped through a per-request
     random permutation of [0, ctx-256) (fixed per request, so low ranks form
     a hot set); the Zipf draws are redrawn every step.  Ids are emitted in
-    random order.
+    random order.  ``layer`` > 0 draws another layer's selections for the
+    same requests (independent streams; layer 0 is the matching workload).
     """
     seed, ctx, K, win = CONFIG_SEEDS["matching"], 65536, 2048, 256
     B, Nq = 8, 1
     topk = np.full((steps, B, Nq, K), -1, np.int32)
     for b in range(B):
-        rng = np.random.default_rng([seed, b])
+        rng = np.random.default_rng([seed, b] if layer == 0 else [seed, b, layer])
         perm = rng.permutation(ctx - win)
         for t in range(steps):
             window, z = _window_plus_zipf(rng, perm, ctx, K, win)
@@ -361,6 +362,24 @@ def gen_reuse(B, reuse, steps=16, name=None, seed=606, K=2048, S=4096):
     return Workload(name, B, Nq, K, S, 1280, steps, seed, topk,
                     np.full((steps, B), ctx, np.int32), np.full(B, ctx, np.int32),
                     np.arange(B, dtype=np.int64) * ctx)
+
+
+def stack_layers(ws, name=None):
+    """One workload whose requests are the (layer, request) pairs of the
+    per-layer workloads ``ws`` (same shapes): each layer keeps its own cache
+    and its own host rows, so the stacked batch is layer-major, B' = L * B,
+    and layer l's rows sit after those of layers < l in one host pool."""
+    w0 = ws[0]
+    L = len(ws)
+    topk = np.concatenate([w.topk for w in ws], axis=1)
+    ctx = np.concatenate([w.ctx_len for w in ws], axis=1)
+    host_rows = np.concatenate([w.host_rows for w in ws])
+    per_layer = w0.host_rows_total
+    row_base = np.concatenate([w.row_base + l * per_layer for l, w in enumerate(ws)])
+    return Workload(name or f"{w0.name}x{L}", w0.B * L, w0.Nq, w0.K, w0.S, w0.row_bytes,
+                    w0.steps, w0.seed, topk, ctx, host_rows.astype(np.int32),
+                    row_base.astype(np.int64), L=w0.L, R=w0.R, a1=w0.a1, a2=w0.a2,
+                    afp=w0.afp)
 
 
 def gen_reuse25_b1(steps=16):
