@@ -105,6 +105,10 @@ def parse():
                     help="instead of the step benchmark: effective host-to-HBM "
                          "bandwidth against row size, zero-copy gather vs one "
                          "hipMemcpyAsync per row vs one bulk copy")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="instead of the step benchmark: threshold prefetch (ECHO) on "
+                         "scored selections: the recall left on the critical path after "
+                         "the exact top-K is known, with and without the prefetch")
     ap.add_argument("--probe-sweep", action="store_true",
                     help="instead of the step benchmark: Stage-One throughput on the "
                          "residency request shape (K=2048, S=8192) at B = 32..512, "
@@ -470,6 +474,91 @@ def transfer_sweep(args):
     return 0
 
 
+def prefetch_mode(args):
+    """Threshold prefetch ahead of the recall (ECHO decode prefetch) on the
+    scored workload (B=8, context 65536, K=2048, S=4096, ~82 % adjacent
+    reuse).  Without prefetch the whole recall (Stage One + gather) follows
+    the top-K.  With it, candidates above the moving-average threshold are
+    matched and copied first (the part that overlaps the indexer), and only
+    the exact selection's continuation is left on the critical path."""
+    import torch
+    import recall_step_amd as r
+    from workloads import make
+
+    torch.cuda.set_device(0)
+    w = make("scored")
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    host = r.HostPool(w.host_bytes)
+    w.fill_host_kv(host.array)
+    cfg = r.avsg_config_default(w.B, 1, w.K, w.S, w.row_bytes)
+    base = r.RecallStep(cfg, host, w.host_rows_total, stream=stream)
+    pre = r.RecallStep(cfg, host, w.host_rows_total, stream=stream)
+    dev = base.Q.device
+    scores = torch.from_numpy(w.extra["scores"]).to(dev)
+    kth = torch.from_numpy(w.extra["kth"]).to(dev)
+    topk = torch.from_numpy(np.ascontiguousarray(w.topk)).to(dev)
+    ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).to(dev)
+    row_base = torch.from_numpy(w.row_base).to(dev)
+    host_rows = torch.from_numpy(w.host_rows).to(dev)
+    theta = torch.full((w.B,), float("inf"), dtype=torch.float32, device=dev)
+    cap = torch.full((w.B,), w.K, dtype=torch.int32, device=dev)  # min(K, N/32) = K here
+    cand = torch.empty((w.B, 1, w.K), dtype=torch.int32, device=dev)
+    o1 = [torch.empty_like(x) for x in (pre.slot_table, pre.hit_mask, pre.n_miss,
+                                        pre.miss_pairs)]
+    io1 = [r.AvsgStepIO(cand.data_ptr(), ctx[t].data_ptr(), row_base.data_ptr(),
+                        host_rows.data_ptr(), o1[0].data_ptr(), o1[1].data_ptr(),
+                        o1[2].data_ptr(), o1[3].data_ptr()) for t in range(w.steps)]
+    iob = [base.io(topk[t], ctx[t], row_base, host_rows) for t in range(w.steps)]
+    iop = [pre.io(topk[t], ctx[t], row_base, host_rows) for t in range(w.steps)]
+    torch.cuda.synchronize()
+    warm = 4
+    rec = []
+    for t in range(w.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        e[0].record(stream)
+        r.avsg_step(base.handle, iob[t], sh)
+        e[1].record(stream)
+        r.avsg_prefetch_select(pre.handle, scores[t].data_ptr(), scores.shape[2],
+                               ctx[t].data_ptr(), theta.data_ptr(), cap.data_ptr(),
+                               cand.data_ptr(), sh)
+        r.avsg_step(pre.handle, io1[t], sh)
+        e[2].record(stream)
+        r.avsg_match_continue(pre.handle, iop[t], sh)
+        r.avsg_gather(pre.handle, iop[t], sh)
+        e[3].record(stream)
+        r.avsg_ema_threshold(pre.handle, kth[t].data_ptr(), theta.data_ptr(), 0.5, sh)
+        e[4].record(stream)
+        torch.cuda.synchronize()
+        n_pre = int(o1[2].sum())
+        n_cand = int((cand >= 0).sum())
+        n_exact = int(pre.n_miss.sum())
+        n_base = int(base.n_miss.sum())
+        rec.append((e[0].elapsed_time(e[1]) * 1e3, e[1].elapsed_time(e[2]) * 1e3,
+                    e[2].elapsed_time(e[3]) * 1e3, n_cand, n_pre, n_exact, n_base))
+    a = np.array(rec[warm:], dtype=np.float64)
+    sel = w.B * w.K
+    out = {
+        "prefetch": "ECHO-style threshold prefetch, scored workload (B=8, K=2048, S=4096, "
+                    "context 65536, ~82% adjacent reuse), alpha 0.5, cap K",
+        "steps": len(a),
+        "no_prefetch_recall_us": round(a[:, 0].mean(), 1),
+        "prefetch_part_us": round(a[:, 1].mean(), 1),
+        "critical_path_recall_us": round(a[:, 2].mean(), 1),
+        "critical_path_speedup": round(a[:, 0].mean() / a[:, 2].mean(), 2),
+        "candidates_per_step": round(a[:, 3].mean(), 1),
+        "rows_prefetched_per_step": round(a[:, 4].mean(), 1),
+        "rows_left_for_exact_recall": round(a[:, 5].mean(), 1),
+        "rows_without_prefetch": round(a[:, 6].mean(), 1),
+        "selected_per_step": sel,
+    }
+    base.close()
+    pre.close()
+    host.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def contiguous_gather_peak(r, torch, stream, row_bytes=1280, rows=1 << 19, blocks=0):
     """The gather kernel on a miss list of consecutive host rows: the
     zero-copy streaming rate of the same kernel without scattered reads."""
@@ -537,6 +626,8 @@ def main():
         return ratios(args)
     if args.layers:
         return layers_mode(args)
+    if args.prefetch:
+        return prefetch_mode(args)
     if args.transfer_sweep:
         return transfer_sweep(args)
     import torch

@@ -233,6 +233,37 @@ int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream);
  * AVSG_FLAG_SKIP_GATHER). */
 int avsg_step(avsg_handle* h, const avsg_step_io* io, void* stream);
 
+/* avsg_match for further query tokens of the step already begun by an
+ * avsg_match call on the same handle: the same Stage One without the
+ * once-per-step lifetime decay.  An avsg_match on tokens A followed by
+ * avsg_match_continue on tokens B equals one avsg_match on the tokens
+ * (A, B) in order whenever no cached or selected id is at or beyond the
+ * verified length N (invalidation runs at the end of each call).  Used to
+ * put prefetched candidates ahead of the exact selection.  AVSG_EINVAL with
+ * AVSG_FLAG_SORT_MERGE (its step-local bookkeeping does not span calls). */
+int avsg_match_continue(avsg_handle* h, const avsg_step_io* io, void* stream);
+
+/* Prefetch candidates (ECHO, decode prefetch: fetch during the indexer pass
+ * every token scoring above a predicted K-th-highest score, at most a cap
+ * proportional to context).  For each request b writes cand[b][0..K): the
+ * first min(cap[b], K) positions j < min(ctx_len[b], row_len), ascending,
+ * whose score scores[b*row_len + j] is strictly above theta[b] (float32
+ * compare), then -1.  cand is meant as the topk of an avsg_match ahead of
+ * the exact selection's avsg_match_continue.  Device pointers: scores float
+ * [B][row_len], ctx_len int32 [B], theta float [B], cap int32 [B], cand
+ * int32 [B][K].  Enqueues one kernel. */
+int avsg_prefetch_select(avsg_handle* h, const float* scores, int64_t row_len,
+                         const int32_t* ctx_len, const float* theta, const int32_t* cap,
+                         int32_t* cand, void* stream);
+
+/* Moving-average threshold for the next step (ECHO: alpha 0.5): for each
+ * request, theta[b] = kth[b] if theta[b] is infinite (no prediction yet),
+ * else alpha*kth[b] + (1 - alpha)*theta[b], each product and the sum rounded
+ * to float32 separately.  kth[b] is the K-th highest score of the step just
+ * selected.  Device pointers float [B]; 0 < alpha <= 1. */
+int avsg_ema_threshold(avsg_handle* h, const float* kth, float* theta, float alpha,
+                       void* stream);
+
 /* Allocate `bytes` of pinned host memory mapped into the device's address
  * space, suitable as host_kv; *out = host address.  Free with
  * avsg_host_free. */

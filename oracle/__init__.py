@@ -36,8 +36,10 @@ RC_NAMES = {0: "ok", -1: "bad argument", -2: "slot referenced earlier in the "
 def build() -> str:
     """Compile the oracle with gcc into ``oracle/liboracle.so``."""
     tmp = _LIB + ".tmp"
+    # -ffp-contract=off: float32 products and sums round one at a time.
     subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror",
-                    "-shared", "-fPIC", "-o", tmp, _SRC], check=True)
+                    "-ffp-contract=off", "-shared", "-fPIC", "-o", tmp, _SRC,
+                    "-lm"], check=True)
     os.replace(tmp, _LIB)
     return _LIB
 
@@ -58,6 +60,10 @@ def _load():
         lib.orc_step_no_reuse.restype = ctypes.c_int
         lib.orc_step_sort_merge.argtypes = [p] * 13
         lib.orc_step_sort_merge.restype = ctypes.c_int
+        lib.orc_prefetch_select.argtypes = [p, p, ctypes.c_int64, p, p, p, p]
+        lib.orc_prefetch_select.restype = None
+        lib.orc_ema_threshold.argtypes = [ctypes.c_int32, p, p, ctypes.c_float]
+        lib.orc_ema_threshold.restype = None
         lib.orc_state_reset.argtypes = [p] * 5
         lib.orc_state_reset.restype = None
         lib.orc_version.restype = ctypes.c_int
@@ -185,6 +191,26 @@ class Oracle:
                                          _ptr(out.miss_pairs))
         if rc != 0:
             raise OracleError(f"oracle step failed: {RC_NAMES.get(rc, rc)}")
+        return out
+
+    def prefetch_select(self, scores, ctx_len, theta, cap) -> np.ndarray:
+        """Prefetch candidates (ECHO decode prefetch), int32 [B][K]: see
+        orc_prefetch_select."""
+        scores = np.ascontiguousarray(scores, np.float32).reshape(self.B, -1)
+        ctx_len = np.ascontiguousarray(ctx_len, np.int32).reshape(self.B)
+        theta = np.ascontiguousarray(theta, np.float32).reshape(self.B)
+        cap = np.ascontiguousarray(cap, np.int32).reshape(self.B)
+        out = np.empty((self.B, self.K), np.int32)
+        _load().orc_prefetch_select(ctypes.byref(self.cfg), _ptr(scores), scores.shape[1],
+                                    _ptr(ctx_len), _ptr(theta), _ptr(cap), _ptr(out))
+        return out
+
+    @staticmethod
+    def ema_threshold(kth, theta, alpha) -> np.ndarray:
+        """Next threshold per request (float32): see orc_ema_threshold."""
+        kth = np.ascontiguousarray(kth, np.float32)
+        out = np.ascontiguousarray(theta, np.float32).copy()
+        _load().orc_ema_threshold(kth.size, _ptr(kth), _ptr(out), float(alpha))
         return out
 
     def probe_buckets(self, x: int) -> list:

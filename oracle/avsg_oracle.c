@@ -48,6 +48,7 @@
  *     Duplicate missing ids within a token set bit 1 and are kept as
  *     separate misses, ordered by (id, position).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -495,6 +496,46 @@ int orc_step_sort_merge(const orc_cfg* cfg, int32_t* Call, int32_t* CNTall,
             }
     }
     return ORC_OK;
+}
+
+/*
+ * Threshold prefetch ahead of the recall (ECHO page, decode prefetch): while
+ * the indexer scores every earlier token, tokens scoring above a predicted
+ * threshold are fetched at once, at most a capped number; the threshold is
+ * a moving average (alpha) of the observed K-th highest scores.
+ * Readings taken: candidates are the first min(cap, K) positions j below
+ * min(N, row_len), in ascending order, with score strictly above theta
+ * (float32); the rest of the row is -1.  The average starts from the first
+ * observed score when theta is infinite.
+ */
+void orc_prefetch_select(const orc_cfg* cfg, const float* scores, int64_t row_len,
+                         const int32_t* ctx_len, const float* theta, const int32_t* cap,
+                         int32_t* cand)
+{
+    for (int32_t b = 0; b < cfg->B; ++b) {
+        int64_t n = ctx_len[b] < 0 ? 0 : ctx_len[b];
+        if (n > row_len) n = row_len;
+        int32_t c = cap[b] < 0 ? 0 : cap[b];
+        if (c > cfg->K) c = cfg->K;
+        int32_t* out = cand + (int64_t)b * cfg->K;
+        int32_t m = 0;
+        for (int64_t j = 0; j < n && m < c; ++j)
+            if (scores[(int64_t)b * row_len + j] > theta[b]) out[m++] = (int32_t)j;
+        for (int32_t i = m; i < cfg->K; ++i) out[i] = -1;
+    }
+}
+
+void orc_ema_threshold(int32_t B, const float* kth, float* theta, float alpha)
+{
+    for (int32_t b = 0; b < B; ++b) {
+        if (isinf(theta[b])) {
+            theta[b] = kth[b];
+        } else {
+            const float p = alpha * kth[b];
+            const float q = (1.0f - alpha) * theta[b];
+            theta[b] = p + q;
+        }
+    }
 }
 
 /* Empty state: no bucket words, no cached ids, all slots dead, counters 0. */

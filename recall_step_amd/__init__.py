@@ -87,6 +87,9 @@ _sigs = {
     "avsg_match": ([_p, ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
     "avsg_gather": ([_p, ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
     "avsg_step": ([_p, ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
+    "avsg_match_continue": ([_p, ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
+    "avsg_prefetch_select": ([_p, _p, ctypes.c_int64, _p, _p, _p, _p, _p], ctypes.c_int),
+    "avsg_ema_threshold": ([_p, _p, _p, ctypes.c_float, _p], ctypes.c_int),
     "avsg_host_alloc": ([ctypes.c_size_t, ctypes.POINTER(_p)], ctypes.c_int),
     "avsg_host_free": ([_p], ctypes.c_int),
 }
@@ -168,6 +171,21 @@ def avsg_gather(h, io: AvsgStepIO, stream) -> None:
 
 def avsg_step(h, io: AvsgStepIO, stream) -> None:
     _check(lib.avsg_step(h, ctypes.byref(io), stream), "avsg_step")
+
+
+def avsg_match_continue(h, io: AvsgStepIO, stream) -> None:
+    _check(lib.avsg_match_continue(h, ctypes.byref(io), stream), "avsg_match_continue")
+
+
+def avsg_prefetch_select(h, scores_ptr, row_len, ctx_len_ptr, theta_ptr, cap_ptr, cand_ptr,
+                         stream) -> None:
+    _check(lib.avsg_prefetch_select(h, scores_ptr, int(row_len), ctx_len_ptr, theta_ptr,
+                                    cap_ptr, cand_ptr, stream), "avsg_prefetch_select")
+
+
+def avsg_ema_threshold(h, kth_ptr, theta_ptr, alpha, stream) -> None:
+    _check(lib.avsg_ema_threshold(h, kth_ptr, theta_ptr, float(alpha), stream),
+           "avsg_ema_threshold")
 
 
 def avsg_host_alloc(nbytes: int) -> int:
@@ -263,6 +281,9 @@ class RecallStep:
 
     def match(self, io: AvsgStepIO, stream=None):
         avsg_match(self.handle, io, _stream_handle(stream))
+
+    def match_continue(self, io: AvsgStepIO, stream=None):
+        avsg_match_continue(self.handle, io, _stream_handle(stream))
 
     def gather(self, io: AvsgStepIO, stream=None):
         avsg_gather(self.handle, io, _stream_handle(stream))

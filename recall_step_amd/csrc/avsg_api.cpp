@@ -198,7 +198,23 @@ int avsg_state_init(avsg_handle* h, const int32_t* row_mask, void* stream) {
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }
 
+namespace {
+int match_impl(avsg_handle* h, const avsg_step_io* io, void* stream, bool predecay);
+}
+
 int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
+    return match_impl(h, io, stream, true);
+}
+
+int avsg_match_continue(avsg_handle* h, const avsg_step_io* io, void* stream) {
+    if (h && (h->cfg.flags & AVSG_FLAG_SORT_MERGE)) return AVSG_EINVAL;
+    return match_impl(h, io, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+int match_impl(avsg_handle* h, const avsg_step_io* io, void* stream, bool predecay) {
     if (!h || !match_io_ok(io)) return AVSG_EINVAL;
     int rc = check_device(h);
     if (rc != AVSG_OK) return rc;
@@ -240,6 +256,7 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
     a.S = c.S;
     a.L = c.L;
     a.R = c.R;
+    a.predecay = predecay ? 1 : 0;
     a.a1 = c.a1;
     a.a2 = c.a2;
     a.afp = c.a_fp;
@@ -249,6 +266,10 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }
+
+}  // namespace
+
+extern "C" {
 
 int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream) {
     if (!h || !gather_io_ok(io, h->cfg.flags)) return AVSG_EINVAL;
@@ -284,6 +305,28 @@ int avsg_step(avsg_handle* h, const avsg_step_io* io, void* stream) {
     if (rc != AVSG_OK) return rc;
     if (h->cfg.flags & AVSG_FLAG_SKIP_GATHER) return AVSG_OK;
     return avsg_gather(h, io, stream);
+}
+
+int avsg_prefetch_select(avsg_handle* h, const float* scores, int64_t row_len,
+                         const int32_t* ctx_len, const float* theta, const int32_t* cap,
+                         int32_t* cand, void* stream) {
+    if (!h || !scores || row_len < 0 || !ctx_len || !theta || !cap || !cand)
+        return AVSG_EINVAL;
+    int rc = check_device(h);
+    if (rc != AVSG_OK) return rc;
+    avsg::PrefetchArgs a{scores, row_len, ctx_len, theta, cap, cand, h->cfg.B, h->cfg.K};
+    hipError_t e = avsg::launch_prefetch_select(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? AVSG_OK : hip_fail(e);
+}
+
+int avsg_ema_threshold(avsg_handle* h, const float* kth, float* theta, float alpha,
+                       void* stream) {
+    if (!h || !kth || !theta || !(alpha > 0.0f && alpha <= 1.0f)) return AVSG_EINVAL;
+    int rc = check_device(h);
+    if (rc != AVSG_OK) return rc;
+    avsg::EmaArgs a{kth, theta, alpha, h->cfg.B};
+    hipError_t e = avsg::launch_ema_threshold(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }
 
 int avsg_host_alloc(size_t bytes, void** out) {

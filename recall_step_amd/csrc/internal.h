@@ -119,6 +119,7 @@ struct Stage1Args {
     int32_t* __restrict__ pairs;
     int64_t host_rows_total;
     int32_t B, Nq, K, S, L, R;
+    int32_t predecay;  // 1: apply the once-per-step lifetime decay first
     uint32_t a1, a2, afp;
 };
 
@@ -165,7 +166,26 @@ int stage1_threads(int K, int requested);
 hipError_t stage1_prepare(size_t lds_bytes);
 hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds_bytes, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s);
+struct PrefetchArgs {
+    const float* __restrict__ scores;  // [B][row_len]
+    int64_t row_len;
+    const int32_t* __restrict__ ctx_len;
+    const float* __restrict__ theta;
+    const int32_t* __restrict__ cap;
+    int32_t* __restrict__ cand;        // [B][K]
+    int32_t B, K;
+};
+
+struct EmaArgs {
+    const float* __restrict__ kth;
+    float* __restrict__ theta;
+    float alpha;
+    int32_t B;
+};
+
 hipError_t launch_offload(const OffloadArgs& a, hipStream_t s);
+hipError_t launch_prefetch_select(const PrefetchArgs& a, hipStream_t s);
+hipError_t launch_ema_threshold(const EmaArgs& a, hipStream_t s);
 hipError_t sort_merge_prepare(size_t lds_bytes);
 hipError_t launch_sort_merge(const Stage1Args& a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_state_init(const InitArgs& a, hipStream_t s);

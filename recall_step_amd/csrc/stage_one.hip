@@ -255,7 +255,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
 
     // Stage the request's state.  The once-per-step decay before the first
     // token is fused into the load: G = max(F - 1, -1) + 1, clamped to
-    // [0, L + 1] for any input.
+    // [0, L + 1] for any input.  A continuation of the step (more query
+    // tokens after an earlier call) stages G = F + 1 without the decay.
+    const int gadd = a.predecay ? 0 : 1;
     for (int j0 = tid; j0 < (S >> 2); j0 += 4 * T) {
         // Loads clamped to the last word (always in bounds), stores guarded.
         int4 q[4], c[4], f[4];
@@ -272,10 +274,10 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             if (j < (S >> 2)) {
                 reinterpret_cast<int4*>(sQ)[j] = q[u];
                 reinterpret_cast<int4*>(sC)[j] = c[u];
-                const uint32_t g0 = uint32_t(min(max(f[u].x, 0), L + 1));
-                const uint32_t g1 = uint32_t(min(max(f[u].y, 0), L + 1));
-                const uint32_t g2 = uint32_t(min(max(f[u].z, 0), L + 1));
-                const uint32_t g3 = uint32_t(min(max(f[u].w, 0), L + 1));
+                const uint32_t g0 = uint32_t(min(max(f[u].x + gadd, 0), L + 1));
+                const uint32_t g1 = uint32_t(min(max(f[u].y + gadd, 0), L + 1));
+                const uint32_t g2 = uint32_t(min(max(f[u].z + gadd, 0), L + 1));
+                const uint32_t g3 = uint32_t(min(max(f[u].w + gadd, 0), L + 1));
                 sGw[j] = g0 | (g1 << 8) | (g2 << 16) | (g3 << 24);
             }
         }

@@ -360,3 +360,117 @@ def test_determinism_repeat_from_same_state():
             assert torch.equal(a, b)
     finally:
         p.close()
+
+
+def test_prefetch_select_and_threshold_match_oracle():
+    """Candidate selection and the moving-average threshold, bit for bit
+    (float32 compare and float32 arithmetic on both sides), over thresholds
+    of +-inf, caps of 0 / small / above K, and lengths beyond the row."""
+    import torch
+    import recall_step_amd as r
+    from oracle import Oracle
+    say("[parity] prefetch select / ema")
+    rng = np.random.default_rng(11)
+    B, K, row = 6, 512, 70000
+    cfg = r.avsg_config_default(B, 1, K, 1024, 16, flags=r.FLAG_SKIP_GATHER)
+    rs = r.RecallStep(cfg, None, 1 << 20)
+    o = Oracle(B, 1, K, 1024, 15, 7, 1, 3, 5, 16, 1)
+    dev = rs.Q.device
+    try:
+        for trial in range(6):
+            sc = rng.standard_normal((B, row)).astype(np.float32)
+            ctx = rng.integers(-5, row + 5000, B).astype(np.int32)
+            theta = rng.normal(2.0, 0.5, B).astype(np.float32)
+            theta[trial % B] = np.inf
+            theta[(trial + 1) % B] = -np.inf
+            cap = rng.choice([0, 7, 200, K, K + 100], B).astype(np.int32)
+            t_sc = torch.from_numpy(sc).to(dev)
+            t_ctx = torch.from_numpy(ctx).to(dev)
+            t_th = torch.from_numpy(theta).to(dev)
+            t_cap = torch.from_numpy(cap).to(dev)
+            cand = torch.empty((B, K), dtype=torch.int32, device=dev)
+            r.avsg_prefetch_select(rs.handle, t_sc.data_ptr(), row, t_ctx.data_ptr(),
+                                   t_th.data_ptr(), t_cap.data_ptr(), cand.data_ptr(), 0)
+            torch.cuda.synchronize()
+            ref = o.prefetch_select(sc, ctx, theta, cap)
+            assert np.array_equal(cand.cpu().numpy(), ref), f"trial {trial}"
+            kth = rng.normal(1.0, 1.0, B).astype(np.float32)
+            for alpha in (0.5, 0.3):
+                r.avsg_ema_threshold(rs.handle, torch.from_numpy(kth).to(dev).data_ptr(),
+                                     t_th.data_ptr(), alpha, 0)
+                torch.cuda.synchronize()
+                theta = Oracle.ema_threshold(kth, theta, alpha)
+                assert np.array_equal(t_th.cpu().numpy(), theta)
+    finally:
+        rs.close()
+
+
+def test_prefetch_then_exact_equals_two_token_step():
+    """Prefetch candidates matched first, then the exact top-K as a
+    continuation of the same step, equal the oracle's one step over the two
+    tokens in that order: outputs of both calls, state, counters and slot
+    buffer after every step; the threshold follows the oracle's average."""
+    import torch
+    import recall_step_amd as r
+    from oracle import Oracle
+    w = make("scored", steps=6, B=4)
+    say("[parity] scored B=4: prefetch + continuation vs 2-token oracle step")
+    host = r.HostPool(w.host_bytes)
+    w.fill_host_kv(host.array)
+    cfg = r.avsg_config_default(w.B, 1, w.K, w.S, w.row_bytes)
+    rs = r.RecallStep(cfg, host, w.host_rows_total)
+    o = Oracle(w.B, 2, w.K, w.S, w.L, w.R, w.a1, w.a2, w.afp, w.row_bytes,
+               w.host_rows_total, host_kv=host.array)
+    dev = rs.Q.device
+    try:
+        scores = torch.from_numpy(w.extra["scores"]).to(dev)
+        kth = torch.from_numpy(w.extra["kth"]).to(dev)
+        topk = torch.from_numpy(np.ascontiguousarray(w.topk)).to(dev)
+        ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).to(dev)
+        row_base = torch.from_numpy(w.row_base).to(dev)
+        host_rows = torch.from_numpy(w.host_rows).to(dev)
+        theta = torch.full((w.B,), float("inf"), dtype=torch.float32, device=dev)
+        cap = torch.full((w.B,), w.K, dtype=torch.int32, device=dev)
+        cand = torch.empty((w.B, 1, w.K), dtype=torch.int32, device=dev)
+        out1 = [torch.empty_like(x) for x in (rs.slot_table, rs.hit_mask, rs.n_miss,
+                                              rs.miss_pairs)]
+        theta_ref = np.full(w.B, np.inf, np.float32)
+        ncand = 0
+        for t in range(w.steps):
+            r.avsg_prefetch_select(rs.handle, scores[t].data_ptr(), scores.shape[2],
+                                   ctx[t].data_ptr(), theta.data_ptr(), cap.data_ptr(),
+                                   cand.data_ptr(), 0)
+            io1 = r.AvsgStepIO(cand.data_ptr(), ctx[t].data_ptr(), row_base.data_ptr(),
+                               host_rows.data_ptr(), out1[0].data_ptr(), out1[1].data_ptr(),
+                               out1[2].data_ptr(), out1[3].data_ptr())
+            rs.match(io1)
+            rs.gather(io1)
+            io2 = rs.io(topk[t], ctx[t], row_base, host_rows)
+            rs.match_continue(io2)
+            rs.gather(io2)
+            r.avsg_ema_threshold(rs.handle, kth[t].data_ptr(), theta.data_ptr(), 0.5, 0)
+            torch.cuda.synchronize()
+            c = o.prefetch_select(w.extra["scores"][t], w.ctx_len[t], theta_ref,
+                                  np.full(w.B, w.K, np.int32))
+            assert np.array_equal(cand.cpu().numpy()[:, 0], c), f"step {t}: candidates"
+            ncand += int((c >= 0).sum())
+            both = np.stack([c, w.topk[t, :, 0]], axis=1)
+            ref = o.step(both, w.ctx_len[t], w.row_base, w.host_rows)
+            for g, outs in ((0, [x.cpu().numpy() for x in out1]),
+                            (1, [x.cpu().numpy() for x in (rs.slot_table, rs.hit_mask,
+                                                           rs.n_miss, rs.miss_pairs)])):
+                assert np.array_equal(outs[0][:, 0], ref.slot_table[:, g]), f"{t}/{g} slots"
+                assert np.array_equal(outs[1][:, 0], ref.hit_mask[:, g]), f"{t}/{g} mask"
+                assert np.array_equal(outs[2][:, 0], ref.n_miss[:, g]), f"{t}/{g} n"
+                for b in range(w.B):
+                    n = int(ref.n_miss[b, g])
+                    assert np.array_equal(outs[3][b, 0, :n], ref.miss_pairs[b, g, :n])
+            for name in ("Q", "C", "F", "CNT"):
+                assert np.array_equal(getattr(rs, name).cpu().numpy(), getattr(o, name)), name
+            assert np.array_equal(rs.dev_kv.cpu().numpy(), o.shadow), f"step {t}: slot buffer"
+            theta_ref = Oracle.ema_threshold(w.extra["kth"][t], theta_ref, 0.5)
+            assert np.array_equal(theta.cpu().numpy(), theta_ref)
+        assert ncand > 0
+    finally:
+        rs.close()
+        host.close()

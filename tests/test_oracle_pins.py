@@ -487,3 +487,63 @@ def test_sort_merge_with_s_equal_k_tracks_adjacent_step_reuse():
             hits = int((outs[t].hit_mask[b, 0] == 1).sum())
             assert hits == np.intersect1d(x, w.topk[t - 1, b, 0]).size
             assert set(before[t][b].tolist()) == set(w.topk[t - 1, b, 0].tolist())
+
+
+# --- threshold prefetch ahead of the recall (ECHO page, decode prefetch) ---
+
+def _prefetch_oracle(B, K):
+    return Oracle(B, 1, K, max(16, 1 << (2 * K - 1).bit_length()), 15, 7, 1, 3, 5, 16, 1)
+
+
+def test_prefetch_extremes():
+    """An infinite threshold prefetches nothing; minus infinity prefetches
+    every position below N up to the cap, in order."""
+    rng = np.random.default_rng(3)
+    o = _prefetch_oracle(3, 64)
+    sc = rng.standard_normal((3, 500)).astype(np.float32)
+    ctx = np.array([500, 40, 300], np.int32)
+    none = o.prefetch_select(sc, ctx, np.full(3, np.inf, np.float32), np.full(3, 64, np.int32))
+    assert (none == -1).all()
+    cap = np.array([64, 64, 10], np.int32)
+    all_ = o.prefetch_select(sc, ctx, np.full(3, -np.inf, np.float32), cap)
+    assert all_[0].tolist() == list(range(64))
+    assert all_[1].tolist() == list(range(40)) + [-1] * 24
+    assert all_[2].tolist() == list(range(10)) + [-1] * 54
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_prefetch_at_the_kplus1_score_is_the_exact_top_k(seed):
+    """With the threshold at the (K+1)-th highest score and cap K, the
+    candidates are exactly the top-K positions (numpy's partition), in
+    ascending order: a perfect prediction prefetches the whole selection."""
+    rng = np.random.default_rng(seed)
+    K, n = 128, 4000
+    o = _prefetch_oracle(2, K)
+    sc = rng.standard_normal((2, n)).astype(np.float32)
+    theta = np.array([np.partition(sc[b], n - K - 1)[n - K - 1] for b in range(2)], np.float32)
+    cand = o.prefetch_select(sc, np.full(2, n, np.int32), theta, np.full(2, K, np.int32))
+    for b in range(2):
+        top = np.sort(np.argpartition(-sc[b], K - 1)[:K])
+        assert np.array_equal(cand[b], top)
+
+
+def test_prefetch_cap_keeps_the_first_positions():
+    rng = np.random.default_rng(9)
+    o = _prefetch_oracle(1, 256)
+    sc = rng.standard_normal((1, 3000)).astype(np.float32)
+    full = o.prefetch_select(sc, [3000], [0.5], [256])[0]
+    capped = o.prefetch_select(sc, [3000], [0.5], [37])[0]
+    assert np.array_equal(capped[:37], full[:37]) and (capped[37:] == -1).all()
+    assert (np.diff(full[full >= 0]) > 0).all()
+
+
+def test_ema_threshold_closes_the_gap_by_one_minus_alpha():
+    """From +inf the first update takes the observed score; with a constant
+    observed score s the gap theta - s shrinks by (1 - alpha) per step."""
+    s = np.array([2.0, -1.5], np.float32)
+    th = Oracle.ema_threshold(s, np.full(2, np.inf, np.float32), 0.5)
+    assert np.array_equal(th, s)
+    th = np.array([10.0, 6.5], np.float32)
+    for n in range(1, 12):
+        th = Oracle.ema_threshold(s, th, 0.5)
+        assert np.allclose(th - s, (np.array([8.0, 8.0]) * 0.5 ** n), rtol=0, atol=1e-6)

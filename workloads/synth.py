@@ -382,6 +382,45 @@ def stack_layers(ws, name=None):
                     afp=w0.afp)
 
 
+def gen_scored(B=8, steps=32, noise=0.3, seed=707):
+    """Indexer scores and their exact top-K, for threshold prefetch (ECHO
+    page, decode prefetch): context 65536, K = 2048, S = 4096 (room for a
+    prefetch token ahead of the exact one), 1280-B rows.
+
+    Each request has a fixed relevance over a random permutation of the
+    context, -0.8 * log(1 + rank / 8) (a hot head and a long tail), plus 10
+    on the 256 most recent tokens.  Step t scores every token as relevance
+    plus Gaussian noise (sd ``noise``, 0.3 giving about 82 % adjacent-step
+    reuse of the top-K, near the 81.61 % the AVSG page reports), in float32.
+    The selection is the exact top-K of the scores (random order), and the
+    K-th highest score is kept for the threshold.
+    """
+    ctx, K, S = 65536, 2048, 4096
+    Nq = 1
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    scores = np.empty((steps, B, ctx), np.float32)
+    kth = np.empty((steps, B), np.float32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b])
+        perm = rng.permutation(ctx)
+        base = np.empty(ctx, np.float32)
+        base[perm] = (-0.8 * np.log1p(np.arange(ctx) / 8.0)).astype(np.float32)
+        base[ctx - 256:] += np.float32(10.0)
+        for t in range(steps):
+            sc = base + (noise * rng.standard_normal(ctx)).astype(np.float32)
+            part = np.argpartition(-sc, K - 1)
+            top = part[:K]
+            scores[t, b] = sc
+            kth[t, b] = sc[part[K - 1]]
+            topk[t, b, 0] = rng.permutation(top)
+    w = Workload("scored", B, Nq, K, S, 1280, steps, seed, topk,
+                 np.full((steps, B), ctx, np.int32), np.full(B, ctx, np.int32),
+                 np.arange(B, dtype=np.int64) * ctx)
+    w.extra["scores"] = scores
+    w.extra["kth"] = kth
+    return w
+
+
 def gen_reuse25_b1(steps=16):
     return gen_reuse(1, 0.25, steps)
 
@@ -393,7 +432,7 @@ def gen_reuse75_b8(steps=16):
 GENERATORS = {"tiny": gen_tiny, "matching": gen_matching,
               "residency": gen_residency, "mtp3": gen_mtp3,
               "imbalanced": gen_imbalanced, "reuse25_b1": gen_reuse25_b1,
-              "reuse75_b8": gen_reuse75_b8}
+              "reuse75_b8": gen_reuse75_b8, "scored": gen_scored}
 
 
 def make(name: str, **kw) -> Workload:
