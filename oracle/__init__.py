@@ -58,6 +58,8 @@ def _load():
         lib.orc_step.restype = ctypes.c_int
         lib.orc_step_no_reuse.argtypes = [p] * 11
         lib.orc_step_no_reuse.restype = ctypes.c_int
+        lib.orc_step_dense.argtypes = [p, p, p, p, p, ctypes.c_int64] + [p] * 10
+        lib.orc_step_dense.restype = ctypes.c_int
         lib.orc_step_sort_merge.argtypes = [p] * 13
         lib.orc_step_sort_merge.restype = ctypes.c_int
         lib.orc_prefetch_select.argtypes = [p, p, ctypes.c_int64, p, p, p, p]
@@ -166,6 +168,32 @@ class Oracle:
                                        _ptr(self.shadow), _ptr(out.slot_table),
                                        _ptr(out.hit_mask), _ptr(out.n_miss),
                                        _ptr(out.miss_pairs))
+        if rc != 0:
+            raise OracleError(f"oracle step failed: {RC_NAMES.get(rc, rc)}")
+        return out
+
+    def step_dense(self, topk, ctx_len, row_base, host_rows, map_len) -> StepOut:
+        """AVSG slot management with an exact id -> slot map instead of the
+        hash table (see orc_step_dense).  The map, int32 [B][map_len], lives
+        in ``self.map`` (created on first use, all -1)."""
+        B, Nq, K = self.B, self.Nq, self.K
+        if getattr(self, "map", None) is None or self.map.shape != (B, map_len):
+            self.map = np.full((B, map_len), -1, np.int32)
+        topk = np.ascontiguousarray(topk, np.int32).reshape(B, Nq, K)
+        ctx_len = np.ascontiguousarray(ctx_len, np.int32).reshape(B)
+        row_base = np.ascontiguousarray(row_base, np.int64).reshape(B)
+        host_rows = np.ascontiguousarray(host_rows, np.int32).reshape(B)
+        out = StepOut(np.empty((B, Nq, K), np.int32), np.empty((B, Nq, K), np.int8),
+                      np.empty((B, Nq), np.int32), np.zeros((B, Nq, K, 2), np.int32))
+        hk = self.host_kv
+        rc = _load().orc_step_dense(ctypes.byref(self.cfg), _ptr(self.C), _ptr(self.F),
+                                    _ptr(self.CNT), _ptr(self.map), int(map_len),
+                                    _ptr(topk), _ptr(ctx_len), _ptr(row_base),
+                                    _ptr(host_rows),
+                                    _ptr(hk) if self.shadow is not None else None,
+                                    _ptr(self.shadow), _ptr(out.slot_table),
+                                    _ptr(out.hit_mask), _ptr(out.n_miss),
+                                    _ptr(out.miss_pairs))
         if rc != 0:
             raise OracleError(f"oracle step failed: {RC_NAMES.get(rc, rc)}")
         return out

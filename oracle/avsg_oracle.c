@@ -333,6 +333,131 @@ int orc_step(const orc_cfg* cfg, int32_t* Qall, int32_t* Call, int32_t* Fall,
 }
 
 /*
+ * AVSG's slot management with a dense id -> slot map in place of the hash
+ * table: the fixed-size integer map tensors of ECHO's GPU cache manager
+ * (host-slot -> GPU-slot map).  Everything but the lookup and the link is
+ * orc_step: pre-decay, refresh to L, ascending misses, least extra decay,
+ * lowest-index dead victims, end-of-step invalidation.  Readings taken:
+ *   - a valid id x (also x < map_len) is a hit iff map[x] >= 0; its slot is
+ *     map[x]; no mapping is ever lost, so there is no collision or
+ *     exhaustion;
+ *   - installing x into slot v first clears the entry of v's old id if it
+ *     still points at v, then sets map[x] = v (so among repeated missing ids
+ *     the larger rank keeps the entry);
+ *   - invalidating slot j clears its id's entry if it points at j.
+ * Q is not used.  Counters as orc_step, with one probe visit per lookup.
+ */
+int orc_step_dense(const orc_cfg* cfg, int32_t* Call, int32_t* Fall, int32_t* CNTall,
+                   int32_t* map_all, int64_t map_len, const int32_t* topk,
+                   const int32_t* ctx_len, const int64_t* row_base,
+                   const int32_t* host_rows, const uint8_t* host_kv, uint8_t* dev_shadow,
+                   int32_t* slot_table, int8_t* hit_mask, int32_t* n_miss,
+                   int32_t* miss_pairs)
+{
+    const int32_t B = cfg->B, Nq = cfg->Nq, K = cfg->K, S = cfg->S, L = cfg->L;
+    if (B < 0 || Nq < 1 || K < 1 || S < 1 || (int64_t)Nq * K > S || L < 1 || L > 127 ||
+        map_len < 1)
+        return ORC_EARG;
+    orc_miss* misses = (orc_miss*)malloc(sizeof(orc_miss) * (size_t)K);
+    int32_t* victims = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+    if (!misses || !victims) { free(misses); free(victims); return ORC_ENOMEM; }
+    int rc = ORC_OK;
+    for (int32_t b = 0; b < B && rc == ORC_OK; ++b) {
+        int32_t* C = Call + (int64_t)b * S;
+        int32_t* F = Fall + (int64_t)b * S;
+        int32_t* map = map_all + (int64_t)b * map_len;
+        int32_t* cnt = CNTall + (int64_t)b * 8;
+        const int row_ok = row_base[b] >= 0 && host_rows[b] >= 0 &&
+                           row_base[b] + host_rows[b] <= cfg->host_rows_total;
+        for (int32_t j = 0; j < S; ++j) F[j] = max32(F[j] - 1, -1);
+        for (int32_t g = 0; g < Nq; ++g) {
+            const int64_t tok = (int64_t)b * Nq + g;
+            const int32_t* X = topk + tok * K;
+            int32_t* O = slot_table + tok * K;
+            int8_t* H = hit_mask + tok * K;
+            int32_t n_valid = 0, n_hit = 0, n_g = 0, live = 0;
+            for (int32_t i = 0; i < K; ++i) {
+                int32_t x = X[i];
+                O[i] = -1; H[i] = -1;
+                if (x == -1) continue;
+                if (!row_ok || x < 0 || x >= host_rows[b] || x >= map_len) {
+                    cnt[ORC_ERRORS] |= 1;
+                    continue;
+                }
+                ++n_valid;
+                if (map[x] >= 0) {
+                    O[i] = map[x]; H[i] = 1; ++n_hit;
+                } else {
+                    misses[n_g].id = x; misses[n_g].pos = i; ++n_g;
+                }
+            }
+            for (int32_t i = 0; i < K; ++i)
+                if (H[i] == 1) F[O[i]] = L;
+            n_miss[tok] = n_g;
+            qsort(misses, (size_t)n_g, sizeof(orc_miss), cmp_miss);
+            for (int32_t r = 1; r < n_g; ++r)
+                if (misses[r].id == misses[r - 1].id) cnt[ORC_ERRORS] |= 2;
+            if (n_g > 0) {
+                int32_t kstar = 0;
+                for (;;) {
+                    int32_t below = 0;
+                    for (int32_t j = 0; j < S; ++j) below += (F[j] < kstar);
+                    if (below >= n_g) break;
+                    ++kstar;
+                }
+                for (int32_t j = 0; j < S; ++j) F[j] = max32(F[j] - kstar, -1);
+                int32_t nv = 0;
+                for (int32_t j = 0; j < S && nv < n_g; ++j)
+                    if (F[j] == -1) victims[nv++] = j;
+                for (int32_t r = 0; r < n_g; ++r) {
+                    const int32_t v = victims[r], x = misses[r].id;
+                    if (C[v] >= 0) {
+                        ++live;
+                        if (C[v] < map_len && map[C[v]] == v) map[C[v]] = -1;
+                    }
+                    C[v] = x;
+                    F[v] = L;
+                    map[x] = v;
+                    O[misses[r].pos] = v;
+                    H[misses[r].pos] = 0;
+                    if (miss_pairs) {
+                        int32_t* mp = miss_pairs + (tok * K + r) * 2;
+                        mp[0] = x;
+                        mp[1] = v;
+                    }
+                }
+            }
+            bump(&cnt[ORC_HITS], n_hit);
+            bump(&cnt[ORC_LOOKUPS], n_valid);
+            bump(&cnt[ORC_MISSES], n_g);
+            bump(&cnt[ORC_LIVE_EVICTIONS], live);
+            bump(&cnt[ORC_PROBE_VISITS], n_valid);
+        }
+        for (int32_t j = 0; j < S; ++j) {
+            if (C[j] >= ctx_len[b]) {
+                if (C[j] < map_len && map[C[j]] == j) map[C[j]] = -1;
+                C[j] = -1;
+            }
+        }
+    }
+    free(misses);
+    free(victims);
+    if (rc == ORC_OK && host_kv && dev_shadow && miss_pairs) {
+        const int64_t rb = cfg->row_bytes;
+        for (int32_t b = 0; b < B; ++b)
+            for (int32_t g = 0; g < Nq; ++g) {
+                const int64_t tok = (int64_t)b * Nq + g;
+                for (int32_t r = 0; r < n_miss[tok]; ++r) {
+                    const int32_t* mp = miss_pairs + (tok * K + r) * 2;
+                    memcpy(dev_shadow + ((int64_t)b * S + mp[1]) * rb,
+                           host_kv + (row_base[b] + mp[0]) * rb, (size_t)rb);
+                }
+            }
+    }
+    return rc;
+}
+
+/*
  * The "KV Offload" configuration the AVSG page compares against (section
  * 4.1): the whole KV cache stays in host memory and every selected entry is
  * transferred at every decode step, with no reuse.  Reading taken: the entry

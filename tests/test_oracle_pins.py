@@ -547,3 +547,104 @@ def test_ema_threshold_closes_the_gap_by_one_minus_alpha():
     for n in range(1, 12):
         th = Oracle.ema_threshold(s, th, 0.5)
         assert np.allclose(th - s, (np.array([8.0, 8.0]) * 0.5 ** n), rtol=0, atol=1e-6)
+
+
+# --- dense id -> slot map (ECHO page, GPU cache manager) -------------------
+
+def _dense_case(seed):
+    rng = np.random.default_rng([21, seed])
+    S = int(rng.choice([16, 32, 64]))
+    Nq = int(rng.integers(1, 4))
+    K = int(rng.integers(1, S // Nq + 1))
+    L = int(rng.choice([1, 2, 3, 5]))
+    univ = int(rng.integers(K, 4 * S + 1))
+    return rng, S, Nq, K, L, univ
+
+
+@pytest.mark.parametrize("chunk", range(6))
+def test_dense_map_equals_dictionary_simulator(chunk):
+    """The dense map is an exact dictionary, so with the same aging policy
+    (AVSG page, sections 3.3 and 3.5) it must equal the dictionary simulator
+    at every step, with several query tokens and with nothing ever lost:
+    slots, hit flags, buffer state and counters."""
+    steps = 0
+    for seed in range(chunk * 50, chunk * 50 + 50):
+        rng, S, Nq, K, L, univ = _dense_case(seed)
+        o = Oracle(1, Nq, K, S, L, 1, 1, 1, 1, 16, univ)
+        sim = DictSim(S, L)
+        for t in range(10):
+            N = int(rng.integers(univ // 2, univ + 1))
+            toks = [rng.choice(univ, K, replace=False).astype(np.int32) for _ in range(Nq)]
+            out = o.step_dense(np.array(toks)[None], np.array([N], np.int32),
+                               np.zeros(1, np.int64), np.array([univ], np.int32), univ)
+            res = sim.step([tk.tolist() for tk in toks], N)
+            for g in range(Nq):
+                for i, x in enumerate(toks[g].tolist()):
+                    assert (int(out.slot_table[0, g, i]), int(out.hit_mask[0, g, i])) == res[g][x]
+                assert out.n_miss[0, g] == sum(1 for v in res[g].values() if v[1] == 0)
+            assert o.C[0].tolist() == sim.C and o.F[0].tolist() == sim.F
+            assert int(o.CNT[0, oracle.LIVE_EVICTIONS]) == sim.live_evictions
+            assert int(o.CNT[0, oracle.LOST_COLLISION]) == int(o.CNT[0, oracle.LOST_EXHAUSTED]) == 0
+            mapped = {x: int(v) for x, v in enumerate(o.map[0].tolist()) if v >= 0}
+            assert mapped == sim.slot_of
+            steps += 1
+    assert steps == 500
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_dense_map_equals_hash_matching_while_nothing_is_lost(seed):
+    """Same allocation and aging (AVSG page, sections 3.3-3.5): while the
+    hash table has lost no mapping it is an exact dictionary too, so both
+    matchers give the same slots, flags, C, F and hit/miss counts."""
+    w = gen_fuzz(seed)
+    h = Oracle.for_workload(w)
+    d = Oracle.for_workload(w)
+    map_len = int(w.host_rows.max())
+    for t in range(w.steps):
+        oh = h.step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
+        od = d.step_dense(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows, map_len)
+        if int(h.CNT[:, oracle.LOST_COLLISION].sum() + h.CNT[:, oracle.LOST_EXHAUSTED].sum()):
+            break
+        assert np.array_equal(oh.slot_table, od.slot_table)
+        assert np.array_equal(oh.hit_mask, od.hit_mask)
+        assert np.array_equal(oh.n_miss, od.n_miss)
+        assert np.array_equal(h.C, d.C) and np.array_equal(h.F, d.F)
+        for k in (oracle.HITS, oracle.LOOKUPS, oracle.MISSES, oracle.LIVE_EVICTIONS,
+                  oracle.ERRORS):
+            assert np.array_equal(h.CNT[:, k], d.CNT[:, k])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_dense_map_points_only_at_slots_that_cache_its_id(seed):
+    """Invariant of the map: an entry x -> v is only ever kept while slot v
+    caches x, and every cached id of a step without repeated ids is mapped
+    (so hits are exactly the selected ids resident before the step)."""
+    w = gen_fuzz(seed)
+    o = Oracle.for_workload(w)
+    map_len = int(w.host_rows.max())
+    for t in range(w.steps):
+        resident = [set(o.C[b][o.C[b] >= 0].tolist()) for b in range(w.B)]
+        out = o.step_dense(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows, map_len)
+        for b in range(w.B):
+            xs = np.flatnonzero(o.map[b] >= 0)
+            assert (o.C[b][o.map[b][xs]] == xs).all()
+            if not (o.CNT[b, oracle.ERRORS] & 2):
+                cached = set(o.C[b][o.C[b] >= 0].tolist())
+                assert cached == set(xs.tolist())
+                if w.Nq == 1:
+                    ids = w.topk[t, b, 0]
+                    for i, x in enumerate(ids.tolist()):
+                        if out.hit_mask[b, 0, i] >= 0:
+                            assert bool(out.hit_mask[b, 0, i]) == (x in resident[b])
+
+
+def test_dense_map_rejects_ids_past_its_length():
+    """An id outside the map is reported like an out-of-range id: slot -1,
+    flag -1 and error bit 1, and nothing is installed for it."""
+    o = _oracle(K=4, S=8)
+    out = o.step_dense(np.array([[[0, 5, 7, -1]]], np.int32), np.array([100], np.int32),
+                       np.zeros(1, np.int64), np.array([100], np.int32), 6)
+    assert out.slot_table[0, 0].tolist() == [0, 1, -1, -1]
+    assert out.hit_mask[0, 0].tolist() == [0, 0, -1, -1]
+    assert o.CNT[0, oracle.ERRORS] == 1 and out.n_miss[0, 0] == 2
+    assert o.map[0].tolist() == [0, -1, -1, -1, -1, 1]
