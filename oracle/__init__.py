@@ -126,6 +126,7 @@ class Oracle:
                    w.row_bytes, w.host_rows_total, host_kv, shadow)
 
     def reset(self):
+        self.map = None
         _load().orc_state_reset(ctypes.byref(self.cfg), _ptr(self.Q), _ptr(self.C),
                                 _ptr(self.F), _ptr(self.CNT))
 

@@ -338,9 +338,11 @@ int orc_step(const orc_cfg* cfg, int32_t* Qall, int32_t* Call, int32_t* Fall,
  * (host-slot -> GPU-slot map).  Everything but the lookup and the link is
  * orc_step: pre-decay, refresh to L, ascending misses, least extra decay,
  * lowest-index dead victims, end-of-step invalidation.  Readings taken:
- *   - a valid id x (also x < map_len) is a hit iff map[x] >= 0; its slot is
- *     map[x]; no mapping is ever lost, so there is no collision or
- *     exhaustion;
+ *   - a valid id x (also x < map_len) is a hit iff m = map[x] is a slot in
+ *     [0, S) that caches x (C[m] == x); its slot is m.  Entries only ever
+ *     point at slots caching their id, so the check never rejects a map this
+ *     step built; it keeps a stale or foreign map harmless.  No mapping is
+ *     lost, so there is no collision or exhaustion;
  *   - installing x into slot v first clears the entry of v's old id if it
  *     still points at v, then sets map[x] = v (so among repeated missing ids
  *     the larger rank keeps the entry);
@@ -385,8 +387,9 @@ int orc_step_dense(const orc_cfg* cfg, int32_t* Call, int32_t* Fall, int32_t* CN
                     continue;
                 }
                 ++n_valid;
-                if (map[x] >= 0) {
-                    O[i] = map[x]; H[i] = 1; ++n_hit;
+                const int32_t m = map[x];
+                if (m >= 0 && m < S && C[m] == x) {
+                    O[i] = m; H[i] = 1; ++n_hit;
                 } else {
                     misses[n_g].id = x; misses[n_g].pos = i; ++n_g;
                 }
@@ -435,7 +438,7 @@ int orc_step_dense(const orc_cfg* cfg, int32_t* Call, int32_t* Fall, int32_t* CN
         }
         for (int32_t j = 0; j < S; ++j) {
             if (C[j] >= ctx_len[b]) {
-                if (C[j] < map_len && map[C[j]] == j) map[C[j]] = -1;
+                if (C[j] >= 0 && C[j] < map_len && map[C[j]] == j) map[C[j]] = -1;
                 C[j] = -1;
             }
         }
