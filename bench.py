@@ -42,7 +42,7 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 
 GATHER_PMC_SUMMARY = os.path.join(ROOT, "profiles", "gather_kernel.matching.pmc.txt")
 GATHER_SOURCES = [os.path.join(ROOT, "recall_step_amd", "csrc", f)
-                  for f in ("gather.hip", "internal.h")]
+                  for f in ("gather.hip", "gather.h")]
 
 
 def gather_source_hash():
@@ -221,10 +221,12 @@ def probe_sweep(args):
 
 def eager_steps(r, torch, stream, w, host, flags, warmup, steps):
     """Run warmup + steps recall steps with an event between Stage One and
-    the gather; returns per-kernel means and the counter deltas."""
+    the gather; returns per-kernel means and the counter deltas.  The dense
+    matcher gets a map of one entry per host row of the longest request."""
     cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
                                 a1=w.a1, a2=w.a2, a_fp=w.afp, flags=flags)
-    rs = r.RecallStep(cfg, host, w.host_rows_total, stream=stream)
+    map_len = int(w.host_rows.max()) if flags & r.FLAG_DENSE_MAP else 0
+    rs = r.RecallStep(cfg, host, w.host_rows_total, stream=stream, map_len=map_len)
     topk = torch.from_numpy(np.ascontiguousarray(w.topk)).cuda()
     ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).cuda()
     row_base = torch.from_numpy(w.row_base).cuda()
@@ -253,7 +255,9 @@ def eager_steps(r, torch, stream, w, host, flags, warmup, steps):
     return {"stage1_us": round(s1, 2), "gather_us": round(g, 2),
             "step_us": round(s1 + g, 2), "rows_per_step": round(misses, 1),
             "gather_GBps": round(misses * w.row_bytes / (g * 1e-6) / 1e9, 2),
-            "hit_rate": round(d[r.CNT_HITS] / max(1, d[r.CNT_LOOKUPS]), 4)}
+            "hit_rate": round(d[r.CNT_HITS] / max(1, d[r.CNT_LOOKUPS]), 4),
+            "lost_per_step": round((d[r.CNT_LOST_COLLISION] + d[r.CNT_LOST_EXHAUSTED]) / steps,
+                                   2)}
 
 
 def ratios(args):
@@ -291,6 +295,7 @@ def ratios(args):
     reuse = eager_steps(r, torch, stream, w, host, 0, 4, 30)
     offload = eager_steps(r, torch, stream, w, host, r.FLAG_NO_REUSE, 4, 30)
     merge = eager_steps(r, torch, stream, w, host, r.FLAG_SORT_MERGE, 4, 30)
+    dense = eager_steps(r, torch, stream, w, host, r.FLAG_DENSE_MAP, 4, 30)
     host.close()
     print(json.dumps({
         "comparison": "matching latency, hash probe vs sort-merge matcher, matching "
@@ -299,6 +304,18 @@ def ratios(args):
         "sort_merge_over_hash": round(merge["stage1_us"] / reuse["stage1_us"], 2),
         "hash_hit_rate": reuse["hit_rate"], "sort_merge_hit_rate": merge["hit_rate"]}),
         flush=True)
+    print(json.dumps({
+        "comparison": "matching latency, hash probe vs dense id-to-slot map, matching "
+                      "workload (B=8, K=S=2048, map of 65536 ids per request)",
+        "hash_stage1_us": reuse["stage1_us"], "dense_stage1_us": dense["stage1_us"],
+        "dense_over_hash": round(dense["stage1_us"] / reuse["stage1_us"], 2),
+        "hash_hit_rate": reuse["hit_rate"], "dense_hit_rate": dense["hit_rate"],
+        "hash_lost_per_step": reuse["lost_per_step"],
+        "hash_step_us": reuse["step_us"], "dense_step_us": dense["step_us"],
+        "hash_rows_per_step": reuse["rows_per_step"],
+        "dense_rows_per_step": dense["rows_per_step"],
+        "state_bytes_per_request": {"hash": 12 * w.S, "dense": 8 * w.S +
+                                    4 * int(w.host_rows.max())}}), flush=True)
     # Matching latency against K at fixed S and against S at fixed K (one
     # request, 75 % adjacent reuse, Stage One only).
     from workloads.synth import gen_reuse
@@ -312,12 +329,15 @@ def ratios(args):
             row[f"K={K_},S={S_}"] = {
                 "hash": eager_steps(r, torch, stream, wk, hk, 0, 4, 12)["stage1_us"],
                 "sort_merge": eager_steps(r, torch, stream, wk, hk, r.FLAG_SORT_MERGE,
-                                          4, 12)["stage1_us"]}
+                                          4, 12)["stage1_us"],
+                "dense": eager_steps(r, torch, stream, wk, hk, r.FLAG_DENSE_MAP,
+                                     4, 12)["stage1_us"]}
             hk.close()
         a, b_ = (row[k] for k in row)
         print(json.dumps({"comparison": f"Stage-One latency scaling, {label}", "us": row,
                           "hash_growth": round(b_["hash"] / a["hash"], 2),
-                          "sort_merge_growth": round(b_["sort_merge"] / a["sort_merge"], 2)}),
+                          "sort_merge_growth": round(b_["sort_merge"] / a["sort_merge"], 2),
+                          "dense_growth": round(b_["dense"] / a["dense"], 2)}),
               flush=True)
     print(json.dumps({
         "comparison": "recall step with reuse vs KV Offload (no reuse), matching workload",

@@ -95,6 +95,25 @@ extern "C" {
                                       no hash table; C as the cached ids, Q
                                       and F untouched; end-of-step
                                       invalidation as usual */
+#define AVSG_FLAG_DENSE_MAP 32u    /* match through a dense id -> slot map
+                                      (avsg_buffers.map) instead of the hash
+                                      table: the fixed-size integer map
+                                      tensors of the GPU cache manager on the
+                                      page "ECHO: Efficient KV Cache
+                                      Offloading with Lossless Prefetching for
+                                      Serving Native Sparse Attention LLMs".
+                                      Aging, victims and invalidation are
+                                      AVSG's; a valid id below map_len is a
+                                      hit iff its entry m is a slot in [0, S)
+                                      that caches it; installs drop the
+                                      victim's old entry if it points at the
+                                      victim and set the new id's entry (the
+                                      largest slot among repeated ids);
+                                      invalidated slots drop their entries.
+                                      No mapping is ever lost; Q is untouched;
+                                      PROBE_VISITS counts one per lookup.
+                                      Ids at or beyond map_len are out of
+                                      range (AVSG_ERR_OUT_OF_RANGE) */
 
 typedef struct avsg_config {
     int32_t B;         /* requests (batch rows), >= 1 */
@@ -138,6 +157,10 @@ typedef struct avsg_buffers {
                           (from avsg_host_alloc or any pinned, device-mapped
                           allocation); may be NULL with AVSG_FLAG_SKIP_GATHER */
     int64_t host_rows_total; /* rows in host_kv */
+    int32_t* map;      /* device int32 [B][map_len], AVSG_FLAG_DENSE_MAP
+                          only (else ignored, may be NULL): map[b][x] = slot
+                          caching id x of request b, -1 = absent */
+    int64_t map_len;   /* ids per map row, >= 1 with AVSG_FLAG_DENSE_MAP */
 } avsg_buffers;
 
 /* Per-step inputs and outputs: device pointers. */
@@ -208,7 +231,7 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs,
 int avsg_destroy(avsg_handle* h);
 
 /* Enqueue a reset of request rows to the empty state: Q = C = F = -1,
- * CNT = 0.  row_mask: device int32 [B], nonzero = reset that row; NULL =
+ * CNT = 0 (and, with AVSG_FLAG_DENSE_MAP, every map entry -1).  row_mask: device int32 [B], nonzero = reset that row; NULL =
  * all rows.  Uses a kernel (no hipMemset). */
 int avsg_state_init(avsg_handle* h, const int32_t* row_mask, void* stream);
 

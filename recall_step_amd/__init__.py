@@ -44,6 +44,7 @@ FLAG_GATHER_BY_REQUEST = 2
 FLAG_GATHER_BY_TOPK = 4
 FLAG_NO_REUSE = 8
 FLAG_SORT_MERGE = 16
+FLAG_DENSE_MAP = 32
 
 
 class AvsgConfig(ctypes.Structure):
@@ -60,7 +61,8 @@ class AvsgBuffers(ctypes.Structure):
     _fields_ = [("Q", ctypes.c_void_p), ("C", ctypes.c_void_p),
                 ("F", ctypes.c_void_p), ("CNT", ctypes.c_void_p),
                 ("dev_kv", ctypes.c_void_p), ("host_kv", ctypes.c_void_p),
-                ("host_rows_total", ctypes.c_int64)]
+                ("host_rows_total", ctypes.c_int64),
+                ("map", ctypes.c_void_p), ("map_len", ctypes.c_int64)]
 
 
 class AvsgStepIO(ctypes.Structure):
@@ -239,7 +241,7 @@ class RecallStep:
     torch device tensors on the current device, plus the handle itself."""
 
     def __init__(self, cfg: AvsgConfig, host: HostPool | None, host_rows_total: int,
-                 stream=None):
+                 stream=None, map_len: int = 0):
         import torch
         dev = torch.device("cuda", torch.cuda.current_device())
         B, Nq, K, S = cfg.B, cfg.N_q, cfg.K, cfg.S
@@ -256,10 +258,14 @@ class RecallStep:
         self.hit_mask = torch.empty((B, Nq, K), dtype=torch.int8, device=dev)
         self.n_miss = torch.empty((B, Nq), dtype=torch.int32, device=dev)
         self.miss_pairs = torch.zeros((B, Nq, K, 2), dtype=torch.int32, device=dev)
+        # The dense matcher's id -> slot map, one row of map_len ids per request.
+        self.map = (torch.empty((B, map_len), dtype=torch.int32, device=dev)
+                    if cfg.flags & FLAG_DENSE_MAP else None)
         self.bufs = AvsgBuffers(_dptr(self.Q), _dptr(self.C), _dptr(self.F),
                                 _dptr(self.CNT), _dptr(self.dev_kv),
                                 host.ptr if host is not None else None,
-                                int(host_rows_total))
+                                int(host_rows_total), _dptr(self.map),
+                                int(map_len) if self.map is not None else 0)
         self.handle = avsg_create(cfg, self.bufs)
         self.state_init(stream=stream)
 

@@ -105,10 +105,12 @@ int avsg_validate_config(const avsg_config* c) {
         return AVSG_EINVAL;
     const uint32_t known = AVSG_FLAG_SKIP_GATHER | AVSG_FLAG_GATHER_BY_REQUEST |
                            AVSG_FLAG_GATHER_BY_TOPK | AVSG_FLAG_NO_REUSE |
-                           AVSG_FLAG_SORT_MERGE;
+                           AVSG_FLAG_SORT_MERGE | AVSG_FLAG_DENSE_MAP;
     if (c->flags & ~known) return AVSG_EINVAL;
-    if ((c->flags & AVSG_FLAG_NO_REUSE) && (c->flags & AVSG_FLAG_SORT_MERGE))
-        return AVSG_EINVAL;
+    // At most one matcher other than the hash table.
+    const uint32_t matchers = c->flags & (AVSG_FLAG_NO_REUSE | AVSG_FLAG_SORT_MERGE |
+                                          AVSG_FLAG_DENSE_MAP);
+    if (matchers & (matchers - 1u)) return AVSG_EINVAL;
     if ((c->flags & AVSG_FLAG_GATHER_BY_REQUEST) && (c->flags & AVSG_FLAG_GATHER_BY_TOPK))
         return AVSG_EINVAL;
     return AVSG_OK;
@@ -138,6 +140,10 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** 
     const bool skip = (cfg->flags & AVSG_FLAG_SKIP_GATHER) != 0;
     if (!skip && (!bufs->host_kv || !aligned16(bufs->host_kv))) return AVSG_EINVAL;
     if (bufs->host_rows_total < 0) return AVSG_EINVAL;
+    const bool dense = (cfg->flags & AVSG_FLAG_DENSE_MAP) != 0;
+    if (dense && (!bufs->map || bufs->map_len < 1 ||
+                  (reinterpret_cast<uintptr_t>(bufs->map) & 3u) != 0))
+        return AVSG_EINVAL;
     if (int64_t(cfg->B) * cfg->N_q > avsg::kMaxTokens) return AVSG_EUNSUPPORTED;
 
     int dev = 0;
@@ -164,6 +170,10 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** 
     if (!h) return AVSG_ENOMEM;
     h->cfg = *cfg;
     h->bufs = *bufs;
+    if (!dense) {
+        h->bufs.map = nullptr;
+        h->bufs.map_len = 0;
+    }
     h->host_dev = host_dev;
     h->device = dev;
     h->lds_bytes = lds;
@@ -193,7 +203,7 @@ int avsg_state_init(avsg_handle* h, const int32_t* row_mask, void* stream) {
     int rc = check_device(h);
     if (rc != AVSG_OK) return rc;
     avsg::InitArgs a{h->bufs.Q, h->bufs.C, h->bufs.F, h->bufs.CNT, row_mask,
-                     h->cfg.B, h->cfg.S};
+                     h->cfg.B, h->cfg.S, h->bufs.map, h->bufs.map_len};
     hipError_t e = avsg::launch_state_init(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }
@@ -260,9 +270,12 @@ int match_impl(avsg_handle* h, const avsg_step_io* io, void* stream, bool predec
     a.a1 = c.a1;
     a.a2 = c.a2;
     a.afp = c.a_fp;
+    a.map = h->bufs.map;
+    a.map_len = h->bufs.map_len;
     hipError_t e = (c.flags & AVSG_FLAG_SORT_MERGE)
                        ? avsg::launch_sort_merge(a, h->lds_bytes, static_cast<hipStream_t>(stream))
                        : avsg::launch_stage1(a, h->stage1_threads, h->lds_bytes,
+                                             (c.flags & AVSG_FLAG_DENSE_MAP) != 0,
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }

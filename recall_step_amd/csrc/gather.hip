@@ -22,7 +22,7 @@
 // top-K position (each token's K positions are cut into equal ranges, one per
 // workgroup, and each range's misses are copied).  Results are identical;
 // only the balance of work across workgroups differs.
-#include "internal.h"
+#include "gather.h"
 
 namespace avsg {
 namespace {
@@ -205,21 +205,6 @@ __global__ __launch_bounds__(T) void gather_by_topk_kernel(GatherArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void state_init_kernel(InitArgs a) {
-    const int b = blockIdx.x;
-    if (a.row_mask && a.row_mask[b] == 0) return;
-    int32_t* q = a.Q + size_t(b) * a.S;
-    int32_t* c = a.C + size_t(b) * a.S;
-    int32_t* f = a.F + size_t(b) * a.S;
-    const int4 neg = make_int4(-1, -1, -1, -1);
-    for (int j = threadIdx.x; j < (a.S >> 2); j += blockDim.x) {
-        reinterpret_cast<int4*>(q)[j] = neg;
-        reinterpret_cast<int4*>(c)[j] = neg;
-        reinterpret_cast<int4*>(f)[j] = neg;
-    }
-    if (threadIdx.x < 8) a.CNT[size_t(b) * 8 + threadIdx.x] = 0;
-}
-
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s) {
@@ -231,11 +216,6 @@ hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s) {
         const size_t lds = size_t(a.B * a.Nq + 1) * sizeof(int32_t);
         hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(T), lds, s, a);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_state_init(const InitArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(state_init_kernel, dim3(a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gather.h"
+
 namespace avsg {
 
 // Stage One runs one workgroup per request of 256, 512 or 1024 threads (by
@@ -22,11 +24,6 @@ constexpr int kHistCopies = 16;
 // the LDS budget and a workgroup has at least 256 threads.
 constexpr int kMaxLifeWords = 16;
 
-// Stage Two: 256-thread workgroups, rows resolved in passes of this size.
-constexpr int kGatherThreads = 256;
-constexpr int kGatherRowsPerPass = 256;
-// Largest B * N_q the gather prologue scans in LDS.
-constexpr int kMaxTokens = 16384;
 
 __host__ __device__ inline int next_pow2(int v) {
     int p = 1;
@@ -121,22 +118,8 @@ struct Stage1Args {
     int32_t B, Nq, K, S, L, R;
     int32_t predecay;  // 1: apply the once-per-step lifetime decay first
     uint32_t a1, a2, afp;
-};
-
-enum GatherMode { kGatherByRow = 0, kGatherByRequest = 1, kGatherByTopk = 2 };
-
-struct GatherArgs {
-    const int32_t* __restrict__ n_miss;
-    const int32_t* __restrict__ pairs;
-    const int32_t* __restrict__ topk;        // by-top-K mode only
-    const int8_t* __restrict__ hit_mask;     // by-top-K mode only
-    const int32_t* __restrict__ slot_table;  // by-top-K mode only
-    const int64_t* __restrict__ row_base;
-    const int32_t* __restrict__ host_rows;
-    const uint8_t* __restrict__ host;  // device alias of the pinned pool
-    uint8_t* __restrict__ dev;
-    int64_t host_rows_total;
-    int32_t B, Nq, K, S, row_bytes, mode;
+    int32_t* __restrict__ map;  // dense matcher only: int32 [B][map_len]
+    int64_t map_len;
 };
 
 struct OffloadArgs {
@@ -159,13 +142,16 @@ struct InitArgs {
     int32_t* CNT;
     const int32_t* row_mask;
     int32_t B, S;
+    int32_t* map;  // NULL unless the dense matcher is configured
+    int64_t map_len;
 };
 
 // Stage-One workgroup size: `requested` if nonzero, else chosen from K.
 int stage1_threads(int K, int requested);
 hipError_t stage1_prepare(size_t lds_bytes);
-hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds_bytes, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& a, int blocks, hipStream_t s);
+// dense: match through the id -> slot map instead of the hash table.
+hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds_bytes, bool dense,
+                         hipStream_t s);
 struct PrefetchArgs {
     const float* __restrict__ scores;  // [B][row_len]
     int64_t row_len;

@@ -126,6 +126,20 @@ __device__ inline int32_t fp_of(uint32_t x, uint32_t afp) {
     return int32_t((x * afp) >> 17);
 }
 
+// Dense-map entries are read and written at L2 (agent scope): the map lives
+// in global memory and its maxima are taken with L2 atomics, so no access may
+// be served from a stale L1 line.
+__device__ inline int32_t map_load(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void map_store(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Drop the entry of id if it still points at slot j.
+__device__ inline void map_clear_if(int32_t* mrow, int64_t map_len, int32_t id, int32_t j) {
+    if (id >= 0 && id < map_len && map_load(mrow + id) == j) map_store(mrow + id, -1);
+}
+
 // 0x80 in every byte of x that is zero, 0 elsewhere (exact for all values).
 __device__ inline uint32_t zero_bytes(uint32_t x) {
     return ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
@@ -210,7 +224,14 @@ __device__ inline void store_outputs(int32_t* __restrict__ O, int8_t* __restrict
     }
 }
 
-template <int T, int IPT>
+// DENSE: the dense id -> slot matcher.  A valid id (also below map_len) is
+// a hit iff its map entry m is a slot in [0, S) that caches it; installs
+// drop the victim's old entry if it still points at the victim, clear every
+// missing id's entry, and after a barrier set it with an atomic maximum of
+// the slot (repeated ids: the largest rank, whose victim is the largest
+// slot, keeps it); invalidated slots drop their entries.  Q is neither read
+// nor written and no bucket is linked.
+template <int T, int IPT, bool DENSE>
 __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int S = a.S, K = a.K, L = a.L, R = a.R;
@@ -252,6 +273,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     int32_t xn[IPT];
     load_ids<IPT>(a.topk + size_t(b) * a.Nq * K, i0, K, vec, xn);
     const int32_t cnt_old = tid < 8 ? a.CNT[size_t(b) * 8 + tid] : 0;
+    int32_t* const mrow = DENSE ? a.map + size_t(b) * size_t(a.map_len) : nullptr;
 
     // Stage the request's state.  The once-per-step decay before the first
     // token is fused into the load: G = max(F - 1, -1) + 1, clamped to
@@ -264,7 +286,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int j = min(j0 + u * T, (S >> 2) - 1);
-            q[u] = reinterpret_cast<const int4*>(gQ)[j];
+            if constexpr (!DENSE) q[u] = reinterpret_cast<const int4*>(gQ)[j];
             c[u] = reinterpret_cast<const int4*>(gC)[j];
             f[u] = reinterpret_cast<const int4*>(gF)[j];
         }
@@ -272,7 +294,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         for (int u = 0; u < 4; ++u) {
             const int j = j0 + u * T;
             if (j < (S >> 2)) {
-                reinterpret_cast<int4*>(sQ)[j] = q[u];
+                if constexpr (!DENSE) reinterpret_cast<int4*>(sQ)[j] = q[u];
                 reinterpret_cast<int4*>(sC)[j] = c[u];
                 const uint32_t g0 = uint32_t(min(max(f[u].x + gadd, 0), L + 1));
                 const uint32_t g1 = uint32_t(min(max(f[u].y + gadd, 0), L + 1));
@@ -319,7 +341,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
 #pragma unroll
         for (int e = 0; e < IPT; ++e) {
             const int32_t v = x[e];
-            const bool ok = v != -1 && row_ok && v >= 0 && v < hr;
+            const bool ok = v != -1 && row_ok && v >= 0 && v < hr && (!DENSE || v < a.map_len);
             if (v != -1 && !ok) c_err |= 1u;
             valid |= uint32_t(ok) << e;
             slot[e] = -1;
@@ -330,7 +352,21 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         // round loaded before any cached id, so the LDS round trips of all
         // IPT ids overlap.
         uint32_t open = valid;
-        for (int t = 0; t <= R; ++t) {
+        if constexpr (DENSE) {
+            int32_t m[IPT], cc[IPT];
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) m[e] = ((valid >> e) & 1u) ? map_load(mrow + x[e]) : -1;
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) cc[e] = (m[e] >= 0 && m[e] < S) ? sC[m[e]] : -2;
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) {
+                const bool hit = ((valid >> e) & 1u) && cc[e] == x[e];
+                slot[e] = hit ? m[e] : slot[e];
+                open &= ~(uint32_t(hit) << e);
+            }
+            c_visit += uint32_t(__popc(valid));
+        }
+        for (int t = 0; t <= (DENSE ? -1 : R); ++t) {
             if (__ballot(open != 0u) == 0ull) break;
             c_visit += uint32_t(__popc(open));
             // Closed ids and empty buckets issue no LDS read.
@@ -530,7 +566,12 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 if (missm & (1u << e)) {
                     const int r = min(max(rank[e], 0), ng - 1);
                     const int32_t v = sVict[r];
-                    if (sC[v] >= 0) ++c_live;
+                    const int32_t old = sC[v];
+                    if (old >= 0) ++c_live;
+                    if constexpr (DENSE) {
+                        map_clear_if(mrow, a.map_len, old, v);
+                        map_store(mrow + x[e], -1);
+                    }
                     sC[v] = x[e];
                     sG[v] = uint8_t(L + 1);
                     slot[e] = v;
@@ -539,52 +580,62 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             }
             __syncthreads();
 
-            // --- Link: first reusable bucket in R+1 rounds, judged on the
-            // bucket words before this token's writes and the slots after its
-            // installs; one scatter, the largest rank keeps a contested bucket.
-            int32_t tgt[IPT];
-            uint32_t lp[IPT], ld[IPT];
+            if constexpr (DENSE) {
 #pragma unroll
-            for (int e = 0; e < IPT; ++e) {
-                tgt[e] = -1;
-                lp[e] = home_bucket(uint32_t(x[e]), a.a1, smask);
-                ld[e] = stride_of(uint32_t(x[e]), a.a2, smask);
-            }
-            uint32_t search = missm;
-            for (int t = 0; t <= R; ++t) {
-                if (__ballot(search != 0u) == 0ull) break;
-                int32_t wd[IPT], cc[IPT];
-#pragma unroll
-                for (int e = 0; e < IPT; ++e) wd[e] = ((search >> e) & 1u) ? sQ[lp[e]] : kEmpty;
-#pragma unroll
-                for (int e = 0; e < IPT; ++e) cc[e] = wd[e] != kEmpty ? sC[wd[e] & int32_t(smask)] : -1;
+                for (int e = 0; e < IPT; ++e)
+                    if (missm & (1u << e))
+                        __hip_atomic_fetch_max(mrow + x[e], slot[e], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                // --- Link: first reusable bucket in R+1 rounds, judged on the
+                // bucket words before this token's writes and the slots after its
+                // installs; one scatter, the largest rank keeps a contested bucket.
+                int32_t tgt[IPT];
+                uint32_t lp[IPT], ld[IPT];
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
-                    const bool reusable = wd[e] == kEmpty || cc[e] == -1 ||
-                                          fp_of(uint32_t(cc[e]), a.afp) != (wd[e] >> 16);
-                    const bool take = ((search >> e) & 1u) && reusable;
-                    tgt[e] = take ? int32_t(lp[e]) : tgt[e];
-                    search &= ~(uint32_t(take) << e);
-                    lp[e] = (lp[e] + ld[e]) & smask;
+                    tgt[e] = -1;
+                    lp[e] = home_bucket(uint32_t(x[e]), a.a1, smask);
+                    ld[e] = stride_of(uint32_t(x[e]), a.a2, smask);
                 }
-            }
-            c_lexh += uint32_t(__popc(search));
-            __syncthreads();
+                uint32_t search = missm;
+                for (int t = 0; t <= R; ++t) {
+                    if (__ballot(search != 0u) == 0ull) break;
+                    int32_t wd[IPT], cc[IPT];
 #pragma unroll
-            for (int e = 0; e < IPT; ++e)
-                if (tgt[e] >= 0) sQ[tgt[e]] = kClaimBase;
-            __syncthreads();
+                    for (int e = 0; e < IPT; ++e)
+                        wd[e] = ((search >> e) & 1u) ? sQ[lp[e]] : kEmpty;
 #pragma unroll
-            for (int e = 0; e < IPT; ++e)
-                if (tgt[e] >= 0) atomicMax(&sQ[tgt[e]], kClaimBase + 1 + rank[e]);
-            __syncthreads();
+                    for (int e = 0; e < IPT; ++e)
+                        cc[e] = wd[e] != kEmpty ? sC[wd[e] & int32_t(smask)] : -1;
 #pragma unroll
-            for (int e = 0; e < IPT; ++e) {
-                if (tgt[e] >= 0) {
-                    if (sQ[tgt[e]] == kClaimBase + 1 + rank[e])
-                        sQ[tgt[e]] = (fp_of(uint32_t(x[e]), a.afp) << 16) | slot[e];
-                    else
-                        ++c_lcol;
+                    for (int e = 0; e < IPT; ++e) {
+                        const bool reusable = wd[e] == kEmpty || cc[e] == -1 ||
+                                              fp_of(uint32_t(cc[e]), a.afp) != (wd[e] >> 16);
+                        const bool take = ((search >> e) & 1u) && reusable;
+                        tgt[e] = take ? int32_t(lp[e]) : tgt[e];
+                        search &= ~(uint32_t(take) << e);
+                        lp[e] = (lp[e] + ld[e]) & smask;
+                    }
+                }
+                c_lexh += uint32_t(__popc(search));
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < IPT; ++e)
+                    if (tgt[e] >= 0) sQ[tgt[e]] = kClaimBase;
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < IPT; ++e)
+                    if (tgt[e] >= 0) atomicMax(&sQ[tgt[e]], kClaimBase + 1 + rank[e]);
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < IPT; ++e) {
+                    if (tgt[e] >= 0) {
+                        if (sQ[tgt[e]] == kClaimBase + 1 + rank[e])
+                            sQ[tgt[e]] = (fp_of(uint32_t(x[e]), a.afp) << 16) | slot[e];
+                        else
+                            ++c_lcol;
+                    }
                 }
             }
 
@@ -611,12 +662,19 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     // write the state back (F = G - 1).
     for (int j = tid; j < (S >> 2); j += T) {
         int4 c = reinterpret_cast<const int4*>(sC)[j];
+        if constexpr (DENSE) {
+            if (c.x >= N) map_clear_if(mrow, a.map_len, c.x, 4 * j);
+            if (c.y >= N) map_clear_if(mrow, a.map_len, c.y, 4 * j + 1);
+            if (c.z >= N) map_clear_if(mrow, a.map_len, c.z, 4 * j + 2);
+            if (c.w >= N) map_clear_if(mrow, a.map_len, c.w, 4 * j + 3);
+        }
         if (c.x >= N) c.x = -1;
         if (c.y >= N) c.y = -1;
         if (c.z >= N) c.z = -1;
         if (c.w >= N) c.w = -1;
         reinterpret_cast<int4*>(gC)[j] = c;
-        reinterpret_cast<int4*>(gQ)[j] = reinterpret_cast<const int4*>(sQ)[j];
+        if constexpr (!DENSE)
+            reinterpret_cast<int4*>(gQ)[j] = reinterpret_cast<const int4*>(sQ)[j];
         const uint32_t w = sGw[j];
         reinterpret_cast<int4*>(gF)[j] =
             make_int4(int(w & 0xFFu) - 1, int((w >> 8) & 0xFFu) - 1,
@@ -648,14 +706,21 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
 }
 
 template <int T, int IPT>
-hipError_t launch_one(const Stage1Args& a, size_t lds, hipStream_t s) {
-    hipLaunchKernelGGL((stage1_kernel<T, IPT>), dim3(a.B), dim3(T), lds, s, a);
+hipError_t launch_one(const Stage1Args& a, size_t lds, bool dense, hipStream_t s) {
+    if (dense)
+        hipLaunchKernelGGL((stage1_kernel<T, IPT, true>), dim3(a.B), dim3(T), lds, s, a);
+    else
+        hipLaunchKernelGGL((stage1_kernel<T, IPT, false>), dim3(a.B), dim3(T), lds, s, a);
     return hipGetLastError();
 }
 
 template <int T, int IPT>
 hipError_t prepare_one(size_t lds) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<T, IPT>),
+    hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<T, IPT, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&stage1_kernel<T, IPT, true>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
 }
 
@@ -687,18 +752,19 @@ hipError_t stage1_prepare(size_t lds) {
 }
 
 template <int T>
-hipError_t launch_t(const Stage1Args& a, size_t lds, hipStream_t s) {
+hipError_t launch_t(const Stage1Args& a, size_t lds, bool dense, hipStream_t s) {
     const int ipt = (a.K + T - 1) / T;
-    if (ipt <= 1) return launch_one<T, 1>(a, lds, s);
-    if (ipt <= 2) return launch_one<T, 2>(a, lds, s);
-    if (ipt <= 4) return launch_one<T, 4>(a, lds, s);
-    return launch_one<T, 8>(a, lds, s);
+    if (ipt <= 1) return launch_one<T, 1>(a, lds, dense, s);
+    if (ipt <= 2) return launch_one<T, 2>(a, lds, dense, s);
+    if (ipt <= 4) return launch_one<T, 4>(a, lds, dense, s);
+    return launch_one<T, 8>(a, lds, dense, s);
 }
 
-hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds, hipStream_t s) {
-    if (threads == 256) return launch_t<256>(a, lds, s);
-    if (threads == 512) return launch_t<512>(a, lds, s);
-    return launch_t<1024>(a, lds, s);
+hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds, bool dense,
+                         hipStream_t s) {
+    if (threads == 256) return launch_t<256>(a, lds, dense, s);
+    if (threads == 512) return launch_t<512>(a, lds, dense, s);
+    return launch_t<1024>(a, lds, dense, s);
 }
 
 }  // namespace avsg

@@ -31,19 +31,24 @@ class Pair:
     """A GPU handle and an oracle on one workload."""
 
     def __init__(self, w, gather=True, gather_blocks=0, shadow=True, stage1_threads=0,
-                 flags=0):
+                 flags=0, map_len=None):
         import torch
         import recall_step_amd as r
         self.r, self.torch, self.w = r, torch, w
         self.gather = gather
         self.no_reuse = bool(flags & r.FLAG_NO_REUSE)
         self.sort_merge = bool(flags & r.FLAG_SORT_MERGE)
+        self.dense = bool(flags & r.FLAG_DENSE_MAP)
+        # Dense matcher: one map entry per host row of the longest request
+        # unless a shorter map is asked for.
+        self.map_len = int(w.host_rows.max()) if map_len is None else int(map_len)
         self.host = r.HostPool(w.host_bytes) if gather else None
         if gather:
             w.fill_host_kv(self.host.array)
         flags |= 0 if gather else r.FLAG_SKIP_GATHER
         self.rs = r.RecallStep(make_cfg(r, w, flags, gather_blocks, stage1_threads),
-                               self.host, w.host_rows_total)
+                               self.host, w.host_rows_total,
+                               map_len=self.map_len if self.dense else 0)
         self.oracle = Oracle.for_workload(
             w, host_kv=self.host.array if gather else None, shadow=shadow and gather)
         dev = self.rs.Q.device
@@ -60,6 +65,9 @@ class Pair:
 
     def oracle_step(self, t):
         w = self.w
+        if self.dense:
+            return self.oracle.step_dense(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows,
+                                          self.map_len)
         step = (self.oracle.step_no_reuse if self.no_reuse else
                 self.oracle.step_sort_merge if self.sort_merge else self.oracle.step)
         return step(w.topk[t], w.ctx_len[t], w.row_base, w.host_rows)
@@ -85,6 +93,8 @@ class Pair:
         assert np.array_equal(rs.C.cpu().numpy(), o.C), f"{ctx}: C"
         assert np.array_equal(rs.F.cpu().numpy(), o.F), f"{ctx}: F"
         assert np.array_equal(rs.CNT.cpu().numpy(), o.CNT), f"{ctx}: CNT"
+        if self.dense:
+            assert np.array_equal(rs.map.cpu().numpy(), o.map), f"{ctx}: map"
         if check_kv:
             assert np.array_equal(rs.dev_kv.cpu().numpy(), o.shadow), f"{ctx}: slot buffer"
 
@@ -95,7 +105,7 @@ class Pair:
 
 
 def run_parity(w, steps=None, kv_every=None, gather=True, gather_blocks=0, label=None,
-               stage1_threads=0, flags=0):
+               stage1_threads=0, flags=0, map_len=None):
     """Step both sides through w, comparing everything after every step;
     returns the oracle's counters, int64 [B][8]."""
     label = label or w.name
@@ -103,7 +113,7 @@ def run_parity(w, steps=None, kv_every=None, gather=True, gather_blocks=0, label
     say(f"[parity] {label}: B={w.B} Nq={w.Nq} K={w.K} S={w.S} L={w.L} R={w.R} "
         f"row={w.row_bytes} host_rows={w.host_rows_total} steps={steps} gather={gather}")
     p = Pair(w, gather=gather, gather_blocks=gather_blocks, stage1_threads=stage1_threads,
-             flags=flags)
+             flags=flags, map_len=map_len)
     try:
         for t in range(steps):
             p.gpu_step(t)

@@ -45,7 +45,8 @@ def test_config_default_values():
 @pytest.mark.parametrize("field,value", [
     ("S", 3000), ("S", 8), ("S", 131072), ("K", 0), ("K", 4096), ("B", 0),
     ("N_q", 0), ("L", 0), ("L", 128), ("R", -1), ("a1", 2), ("a2", 4),
-    ("a_fp", 0), ("row_bytes", 1000), ("row_bytes", 0), ("flags", 32), ("flags", 6), ("flags", 24),
+    ("a_fp", 0), ("row_bytes", 1000), ("row_bytes", 0), ("flags", 64), ("flags", 6),
+    ("flags", 24), ("flags", 40), ("flags", 48),
     ("gather_blocks", -1), ("stage1_threads", 128), ("stage1_threads", 300),
     ("stage1_threads", 2048)])
 def test_invalid_configs_rejected(field, value):
@@ -92,6 +93,12 @@ def test_create_rejects_bad_arguments_before_touching_a_device():
     c.S = 16
     with pytest.raises(r.AvsgError):
         r.avsg_create(c, r.AvsgBuffers(17, 32, 48, 64, 80, 96, 1))
+    # the dense matcher needs its map (non-NULL, 4-byte aligned, map_len >= 1)
+    c.flags = r.FLAG_DENSE_MAP
+    for m, n in ((None, 100), (64, 0), (66, 100)):
+        with pytest.raises(r.AvsgError) as e:
+            r.avsg_create(c, r.AvsgBuffers(16, 32, 48, 64, 80, 96, 1, m, n))
+        assert e.value.code == r.AVSG_EINVAL
 
 
 def test_null_safe_destroy_and_free():

@@ -474,3 +474,117 @@ def test_prefetch_then_exact_equals_two_token_step():
     finally:
         rs.close()
         host.close()
+
+
+# --- dense id -> slot map matcher (ECHO page, GPU cache manager) -----------
+
+def test_dense_map_on_fuzz_corpus():
+    """The dense matcher against its oracle on tiny random cases (padding,
+    out-of-range and speculative ids, MTP), with a map covering every host
+    row and with one covering half of them (ids past it are out of range)."""
+    import recall_step_amd as r
+    for seed in range(0, 160, 4):
+        w = gen_fuzz(seed)
+        run_parity(w, kv_every=1, flags=r.FLAG_DENSE_MAP, label=f"fuzz {seed} dense")
+        run_parity(gen_fuzz(seed), flags=r.FLAG_DENSE_MAP | r.FLAG_GATHER_BY_TOPK,
+                   map_len=max(1, int(w.host_rows.max()) // 2), label=f"fuzz {seed} dense half")
+
+
+@pytest.mark.parametrize("name", ["matching", "residency", "mtp3", "imbalanced"])
+def test_dense_map_on_workloads(name):
+    import recall_step_amd as r
+    w = make(name, steps=6) if name != "mtp3" else make(name, steps=4, B=4)
+    cnt = run_parity(w, kv_every=3, flags=r.FLAG_DENSE_MAP, label=f"{name} dense").sum(0)
+    assert cnt[0] > 0 and cnt[3] == cnt[4] == 0
+
+
+@pytest.mark.parametrize("threads", [256, 512])
+def test_dense_map_workgroup_size_does_not_change_results(threads):
+    import recall_step_amd as r
+    run_parity(make("matching", steps=4), gather=False, stage1_threads=threads,
+               flags=r.FLAG_DENSE_MAP, label=f"matching dense T={threads}")
+
+
+def test_dense_map_repeated_missing_ids():
+    """Repeated missing ids take the sorting path and several slots; the
+    map keeps the largest of them."""
+    import recall_step_amd as r
+
+    def draw(rng, t, b):
+        ids = rng.choice(50000, 700, replace=False)
+        dup = rng.choice(ids, 20, replace=False)
+        return rng.permutation(np.concatenate([ids, dup])).astype(np.int32)
+
+    w = _stage_one_only("repeated ids dense", 720, 2048, 5, 2, 50000, draw)
+    cnt = run_parity(w, gather=False, flags=r.FLAG_DENSE_MAP)
+    assert (cnt[:, 6] & 2).all()
+
+
+def test_dense_map_state_init_resets_map_rows():
+    import torch
+    import recall_step_amd as r
+    w = make("residency", steps=6, B=3)
+    say("[parity] dense state_init row mask")
+    p = Pair(w, flags=r.FLAG_DENSE_MAP)
+    try:
+        for t in range(w.steps):
+            if t == 3:
+                mask = torch.tensor([1, 0, 1], dtype=torch.int32, device=p.rs.Q.device)
+                p.rs.state_init(mask)
+                for b in (0, 2):
+                    p.oracle.C[b] = p.oracle.F[b] = p.oracle.Q[b] = -1
+                    p.oracle.CNT[b] = 0
+                    p.oracle.map[b] = -1
+            p.gpu_step(t)
+            p.compare(p.oracle_step(t), f"dense row reset step {t}", check_kv=True)
+    finally:
+        p.close()
+
+
+def test_dense_map_continuation_equals_two_token_step():
+    """avsg_match on tokens A then avsg_match_continue on tokens B equal the
+    oracle's one dense step over (A, B) when no id reaches the verified
+    length, map included."""
+    import torch
+    import recall_step_amd as r
+    from oracle import Oracle
+    w = make("residency", steps=6, B=4)
+    assert (w.topk < w.ctx_len[:, :, None, None]).all()
+    say("[parity] residency B=4 dense: match + continuation vs 2-token oracle step")
+    map_len = int(w.host_rows.max())
+    host = r.HostPool(w.host_bytes)
+    w.fill_host_kv(host.array)
+    cfg = r.avsg_config_default(w.B, 1, w.K, w.S, w.row_bytes, L=w.L, R=w.R, a1=w.a1,
+                                a2=w.a2, a_fp=w.afp, flags=r.FLAG_DENSE_MAP)
+    rs = r.RecallStep(cfg, host, w.host_rows_total, map_len=map_len)
+    o = Oracle(w.B, 2, w.K, w.S, w.L, w.R, w.a1, w.a2, w.afp, w.row_bytes,
+               w.host_rows_total, host_kv=host.array)
+    dev = rs.Q.device
+    try:
+        topk = torch.from_numpy(np.ascontiguousarray(w.topk)).to(dev)
+        ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).to(dev)
+        row_base = torch.from_numpy(w.row_base).to(dev)
+        host_rows = torch.from_numpy(w.host_rows).to(dev)
+        for t in range(w.steps):
+            u = (t + 3) % w.steps
+            io1 = rs.io(topk[t], ctx[t], row_base, host_rows)
+            rs.step(io1)
+            torch.cuda.synchronize()
+            first = [x.cpu().numpy() for x in (rs.slot_table, rs.hit_mask, rs.n_miss)]
+            io2 = rs.io(topk[u], ctx[t], row_base, host_rows)
+            rs.match_continue(io2)
+            rs.gather(io2)
+            torch.cuda.synchronize()
+            second = [x.cpu().numpy() for x in (rs.slot_table, rs.hit_mask, rs.n_miss)]
+            both = np.concatenate([w.topk[t], w.topk[u]], axis=1)
+            ref = o.step_dense(both, w.ctx_len[t], w.row_base, w.host_rows, map_len)
+            for g, outs in ((0, first), (1, second)):
+                assert np.array_equal(outs[0][:, 0], ref.slot_table[:, g]), f"{t}/{g} slots"
+                assert np.array_equal(outs[1][:, 0], ref.hit_mask[:, g]), f"{t}/{g} mask"
+                assert np.array_equal(outs[2][:, 0], ref.n_miss[:, g]), f"{t}/{g} n"
+            for name in ("C", "F", "CNT", "map"):
+                assert np.array_equal(getattr(rs, name).cpu().numpy(), getattr(o, name)), name
+            assert np.array_equal(rs.dev_kv.cpu().numpy(), o.shadow), f"step {t}: slot buffer"
+    finally:
+        rs.close()
+        host.close()
