@@ -317,8 +317,12 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     const int dw0 = tid * D;
     const int dwn = dw0 < nd ? D : 0;
 
-    uint32_t c_hits = 0, c_look = 0, c_lcol = 0, c_lexh = 0, c_live = 0, c_visit = 0;
-    uint32_t c_err = 0, c_miss = 0;
+    // Counters: c_hits, c_look and c_miss are workgroup totals (the same in
+    // every thread); c_lcol, c_lexh and c_live are wave totals (from
+    // ballots); c_visit is per thread.
+    uint32_t c_hits = 0, c_look = 0, c_miss = 0;
+    uint32_t c_lcol = 0, c_lexh = 0, c_live = 0;
+    uint32_t c_visit = 0, c_err = 0;
 
     __syncthreads();
 
@@ -350,7 +354,10 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         }
         // Rounds in lock step over the thread's ids, every bucket word of a
         // round loaded before any cached id, so the LDS round trips of all
-        // IPT ids overlap.
+        // IPT ids overlap.  Every read is issued for every id (bucket and
+        // slot indices are always in [0, S)) and the open mask selects the
+        // results afterwards: branch-free rounds cost fewer instructions than
+        // masking each read.
         uint32_t open = valid;
         if constexpr (DENSE) {
             int32_t m[IPT], cc[IPT];
@@ -369,12 +376,11 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         for (int t = 0; t <= (DENSE ? -1 : R); ++t) {
             if (__ballot(open != 0u) == 0ull) break;
             c_visit += uint32_t(__popc(open));
-            // Closed ids and empty buckets issue no LDS read.
             int32_t wd[IPT], cc[IPT];
 #pragma unroll
-            for (int e = 0; e < IPT; ++e) wd[e] = ((open >> e) & 1u) ? sQ[pos[e]] : kEmpty;
+            for (int e = 0; e < IPT; ++e) wd[e] = sQ[pos[e]];
 #pragma unroll
-            for (int e = 0; e < IPT; ++e) cc[e] = wd[e] != kEmpty ? sC[wd[e] & int32_t(smask)] : -2;
+            for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
 #pragma unroll
             for (int e = 0; e < IPT; ++e) {
                 const bool hit = ((open >> e) & 1u) && wd[e] != kEmpty && cc[e] == x[e];
@@ -396,12 +402,15 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             }
         }
         const int m_local = __popc(missm);
-        c_look += uint32_t(__popc(valid));
-        c_hits += uint32_t(__popc(valid & ~missm));
 
-        int ng, idlo, idhi;
-        block_sum_min_max<T>(m_local, lo_local, hi_local, sMM, &ng, &idlo, &idhi);
-        ng = min(ng, K);
+        // Miss and valid-id totals in one sum (each at most K < 2^16).
+        int nsum, idlo, idhi;
+        block_sum_min_max<T>(m_local | (__popc(valid) << 16), lo_local, hi_local, sMM, &nsum,
+                             &idlo, &idhi);
+        const int ng = min(nsum & 0xFFFF, K);
+        const int nvalid = nsum >> 16;
+        c_look += uint32_t(nvalid);
+        c_hits += uint32_t(nvalid - ng);
         c_miss += uint32_t(ng);
 
         // --- Rank of each miss among the token's misses, ascending id ------
@@ -491,25 +500,21 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             // --- Pass 3: victims ---------------------------------------------
             // Dead slots now; if fewer than ng, the least extra decay k* with
             // #{F < k*} >= ng, applied to every slot.
-            uint32_t gw[kMaxLifeWords];
-#pragma unroll
-            for (int q = 0; q < kMaxLifeWords; ++q) gw[q] = q < dwn ? sGw[dw0 + q] : ~0u;
+            // Each thread reads its own lifetime words from LDS in every pass
+            // (loops bounded by its word count; no register copy).
             int dead_local = 0;
-#pragma unroll
-            for (int q = 0; q < kMaxLifeWords; ++q) dead_local += __popc(zero_bytes(gw[q]));
+            for (int q = 0; q < dwn; ++q) dead_local += __popc(zero_bytes(sGw[dw0 + q]));
             int dead_total;
             int doff = block_excl_scan<T>(dead_local, sS0, &dead_total);
             if (dead_total < ng) {
                 // Histogram of G over 16 LDS copies (lane % 16 picks one).
                 int32_t* hc = sHist + (lane & (kHistCopies - 1)) * HB;
-#pragma unroll
-                for (int q = 0; q < kMaxLifeWords; ++q) {
-                    if (q < dwn) {
-                        atomicAdd(&hc[gw[q] & 0xFFu], 1);
-                        atomicAdd(&hc[(gw[q] >> 8) & 0xFFu], 1);
-                        atomicAdd(&hc[(gw[q] >> 16) & 0xFFu], 1);
-                        atomicAdd(&hc[gw[q] >> 24], 1);
-                    }
+                for (int q = 0; q < dwn; ++q) {
+                    const uint32_t gq = sGw[dw0 + q];
+                    atomicAdd(&hc[gq & 0xFFu], 1);
+                    atomicAdd(&hc[(gq >> 8) & 0xFFu], 1);
+                    atomicAdd(&hc[(gq >> 16) & 0xFFu], 1);
+                    atomicAdd(&hc[gq >> 24], 1);
                 }
                 __syncthreads();
                 if (tid < 64) {
@@ -530,54 +535,52 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 __syncthreads();
                 const uint32_t kstar = uint32_t(sMisc[1]);
                 dead_local = 0;
+                for (int q = 0; q < dwn; ++q) {
+                    const uint32_t gq = sGw[dw0 + q];
+                    uint32_t r = 0;
 #pragma unroll
-                for (int q = 0; q < kMaxLifeWords; ++q) {
-                    if (q < dwn) {
-                        uint32_t r = 0;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t v = (gw[q] >> (8 * j)) & 0xFFu;
-                            r |= (v > kstar ? v - kstar : 0u) << (8 * j);
-                        }
-                        gw[q] = r;
-                        sGw[dw0 + q] = r;
-                        dead_local += __popc(zero_bytes(r));
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t v = (gq >> (8 * j)) & 0xFFu;
+                        r |= (v > kstar ? v - kstar : 0u) << (8 * j);
                     }
+                    sGw[dw0 + q] = r;
+                    dead_local += __popc(zero_bytes(r));
                 }
                 doff = block_excl_scan<T>(dead_local, sS1, &dead_total);
             }
             // CollectDead: the ng lowest-index dead slots, in slot order.
-#pragma unroll
-            for (int q = 0; q < kMaxLifeWords; ++q) {
-                if (q < dwn && doff < ng) {
-                    uint32_t z = zero_bytes(gw[q]);
-                    while (z && doff < ng) {
-                        const int j = (__ffs(int(z)) - 1) >> 3;
-                        sVict[doff++] = (dw0 + q) * 4 + j;
-                        z &= z - 1u;
-                    }
+            for (int q = 0; q < dwn && doff < ng; ++q) {
+                uint32_t z = zero_bytes(sGw[dw0 + q]);
+                while (z && doff < ng) {
+                    const int j = (__ffs(int(z)) - 1) >> 3;
+                    sVict[doff++] = (dw0 + q) * 4 + j;
+                    z &= z - 1u;
                 }
             }
             __syncthreads();
 
             // --- Install the r-th smallest miss into the r-th victim ---------
+            uint32_t livem = 0;
 #pragma unroll
             for (int e = 0; e < IPT; ++e) {
                 if (missm & (1u << e)) {
                     const int r = min(max(rank[e], 0), ng - 1);
                     const int32_t v = sVict[r];
                     const int32_t old = sC[v];
-                    if (old >= 0) ++c_live;
+                    livem |= uint32_t(old >= 0) << e;
                     if constexpr (DENSE) {
                         map_clear_if(mrow, a.map_len, old, v);
                         map_store(mrow + x[e], -1);
                     }
                     sC[v] = x[e];
+                    gC[v] = x[e];  // written through: C is not written back in full
                     sG[v] = uint8_t(L + 1);
                     slot[e] = v;
                     sPair[r] = make_int2(x[e], v);
                 }
             }
+#pragma unroll
+            for (int e = 0; e < IPT; ++e) c_live += uint32_t(__popcll(__ballot((livem >> e) & 1u)));
             __syncthreads();
 
             if constexpr (DENSE) {
@@ -603,11 +606,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                     if (__ballot(search != 0u) == 0ull) break;
                     int32_t wd[IPT], cc[IPT];
 #pragma unroll
-                    for (int e = 0; e < IPT; ++e)
-                        wd[e] = ((search >> e) & 1u) ? sQ[lp[e]] : kEmpty;
+                    for (int e = 0; e < IPT; ++e) wd[e] = sQ[lp[e]];
 #pragma unroll
-                    for (int e = 0; e < IPT; ++e)
-                        cc[e] = wd[e] != kEmpty ? sC[wd[e] & int32_t(smask)] : -1;
+                    for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
 #pragma unroll
                     for (int e = 0; e < IPT; ++e) {
                         const bool reusable = wd[e] == kEmpty || cc[e] == -1 ||
@@ -618,7 +619,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                         lp[e] = (lp[e] + ld[e]) & smask;
                     }
                 }
-                c_lexh += uint32_t(__popc(search));
+#pragma unroll
+                for (int e = 0; e < IPT; ++e)
+                    c_lexh += uint32_t(__popcll(__ballot((search >> e) & 1u)));
                 __syncthreads();
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
@@ -628,15 +631,22 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 for (int e = 0; e < IPT; ++e)
                     if (tgt[e] >= 0) atomicMax(&sQ[tgt[e]], kClaimBase + 1 + rank[e]);
                 __syncthreads();
+                uint32_t lostm = 0;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
                     if (tgt[e] >= 0) {
-                        if (sQ[tgt[e]] == kClaimBase + 1 + rank[e])
-                            sQ[tgt[e]] = (fp_of(uint32_t(x[e]), a.afp) << 16) | slot[e];
-                        else
-                            ++c_lcol;
+                        if (sQ[tgt[e]] == kClaimBase + 1 + rank[e]) {
+                            const int32_t word = (fp_of(uint32_t(x[e]), a.afp) << 16) | slot[e];
+                            sQ[tgt[e]] = word;
+                            gQ[tgt[e]] = word;  // written through, like C
+                        } else {
+                            lostm |= 1u << e;
+                        }
                     }
                 }
+#pragma unroll
+                for (int e = 0; e < IPT; ++e)
+                    c_lcol += uint32_t(__popcll(__ballot((lostm >> e) & 1u)));
             }
 
             // Miss list (id, slot) in rank order.
@@ -658,46 +668,47 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         __syncthreads();
     }
 
-    // End of step: empty every slot caching a speculative id (>= N), then
-    // write the state back (F = G - 1).
+    // End of step: empty every slot caching a speculative id (>= N) and
+    // write the lifetimes back (F = G - 1).  Installs and links wrote C and Q
+    // through to global memory as they happened, so only the emptied slots
+    // are written here.
     for (int j = tid; j < (S >> 2); j += T) {
-        int4 c = reinterpret_cast<const int4*>(sC)[j];
-        if constexpr (DENSE) {
-            if (c.x >= N) map_clear_if(mrow, a.map_len, c.x, 4 * j);
-            if (c.y >= N) map_clear_if(mrow, a.map_len, c.y, 4 * j + 1);
-            if (c.z >= N) map_clear_if(mrow, a.map_len, c.z, 4 * j + 2);
-            if (c.w >= N) map_clear_if(mrow, a.map_len, c.w, 4 * j + 3);
+        const int4 c = reinterpret_cast<const int4*>(sC)[j];
+        const int32_t cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (cv[u] >= N) {
+                if constexpr (DENSE) map_clear_if(mrow, a.map_len, cv[u], 4 * j + u);
+                gC[4 * j + u] = -1;
+            }
         }
-        if (c.x >= N) c.x = -1;
-        if (c.y >= N) c.y = -1;
-        if (c.z >= N) c.z = -1;
-        if (c.w >= N) c.w = -1;
-        reinterpret_cast<int4*>(gC)[j] = c;
-        if constexpr (!DENSE)
-            reinterpret_cast<int4*>(gQ)[j] = reinterpret_cast<const int4*>(sQ)[j];
         const uint32_t w = sGw[j];
         reinterpret_cast<int4*>(gF)[j] =
             make_int4(int(w & 0xFFu) - 1, int((w >> 8) & 0xFFu) - 1,
                       int((w >> 16) & 0xFFu) - 1, int(w >> 24) - 1);
     }
 
-    // Counters: wave sums, then one LDS atomic per wave and counter.
+    // Counters: one wave sum (visits), then one LDS atomic per wave for
+    // each counter kept per wave.
     int32_t* sCnt = sMisc + 2;
     if (tid < 8) sCnt[tid] = 0;
     __syncthreads();
-    const uint32_t vals[6] = {c_hits, c_look, c_lcol, c_lexh, c_live, c_visit};
-    const int idx[6] = {0, 1, 3, 4, 5, 7};
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
-        const int s = lane63(wave_scan_add(int(vals[k])));
-        if (lane == 0 && s) atomicAdd(&sCnt[idx[k]], s);
-    }
+    const int visits = lane63(wave_scan_add(int(c_visit)));
     const uint64_t e1 = __ballot(c_err & 1u), e2 = __ballot(c_err & 2u);
-    if (lane == 0 && (e1 || e2)) atomicOr(&sCnt[6], (e1 ? 1 : 0) | (e2 ? 2 : 0));
+    if (lane == 0) {
+        if (c_lcol) atomicAdd(&sCnt[3], int(c_lcol));
+        if (c_lexh) atomicAdd(&sCnt[4], int(c_lexh));
+        if (c_live) atomicAdd(&sCnt[5], int(c_live));
+        if (visits) atomicAdd(&sCnt[7], visits);
+        if (e1 || e2) atomicOr(&sCnt[6], (e1 ? 1 : 0) | (e2 ? 2 : 0));
+    }
     __syncthreads();
     if (tid < 8) {
         int32_t* cnt = a.CNT + size_t(b) * 8;
-        const uint32_t add = tid == 2 ? c_miss : uint32_t(sCnt[tid]);
+        const uint32_t add = tid == 0   ? c_hits
+                             : tid == 1 ? c_look
+                             : tid == 2 ? c_miss
+                                        : uint32_t(sCnt[tid]);
         if (tid == 6)
             cnt[6] = cnt_old | int32_t(add);
         else
