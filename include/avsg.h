@@ -26,7 +26,9 @@
  *    given at capture time.
  *  - Bad device data never faults: an id outside a request's host rows is
  *    treated as padding and sets AVSG_ERR_OUT_OF_RANGE in that request's
- *    error counter.
+ *    error counter.  The state buffers (Q, C, F, and the map) must hold what
+ *    avsg_state_init and earlier steps wrote; other contents give
+ *    unspecified results, with every access still in bounds.
  */
 #ifndef AVSG_H
 #define AVSG_H

@@ -381,13 +381,19 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             for (int e = 0; e < IPT; ++e) wd[e] = sQ[pos[e]];
 #pragma unroll
             for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
+            // Hit bits of every id first, masked by the open ids after, so
+            // that no read is moved under a branch.
+            uint32_t hitm = 0;
+#pragma unroll
+            for (int e = 0; e < IPT; ++e)
+                hitm |= uint32_t((wd[e] != kEmpty) & (cc[e] == x[e])) << e;
+            hitm &= open;
 #pragma unroll
             for (int e = 0; e < IPT; ++e) {
-                const bool hit = ((open >> e) & 1u) && wd[e] != kEmpty && cc[e] == x[e];
-                slot[e] = hit ? (wd[e] & int32_t(smask)) : slot[e];
-                open &= ~(uint32_t(hit) << e);
+                slot[e] = ((hitm >> e) & 1u) ? (wd[e] & int32_t(smask)) : slot[e];
                 pos[e] = (pos[e] + dst[e]) & smask;
             }
+            open &= ~hitm;
         }
         // open now holds exactly the valid misses.
         const uint32_t missm = open;
@@ -609,33 +615,36 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                     for (int e = 0; e < IPT; ++e) wd[e] = sQ[lp[e]];
 #pragma unroll
                     for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
+                    uint32_t takem = 0;
+#pragma unroll
+                    for (int e = 0; e < IPT; ++e)
+                        takem |= uint32_t((wd[e] == kEmpty) | (cc[e] == -1) |
+                                          (fp_of(uint32_t(cc[e]), a.afp) != (wd[e] >> 16)))
+                                 << e;
+                    takem &= search;
 #pragma unroll
                     for (int e = 0; e < IPT; ++e) {
-                        const bool reusable = wd[e] == kEmpty || cc[e] == -1 ||
-                                              fp_of(uint32_t(cc[e]), a.afp) != (wd[e] >> 16);
-                        const bool take = ((search >> e) & 1u) && reusable;
-                        tgt[e] = take ? int32_t(lp[e]) : tgt[e];
-                        search &= ~(uint32_t(take) << e);
+                        tgt[e] = ((takem >> e) & 1u) ? int32_t(lp[e]) : tgt[e];
                         lp[e] = (lp[e] + ld[e]) & smask;
                     }
+                    search &= ~takem;
                 }
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
                     c_lexh += uint32_t(__popcll(__ballot((search >> e) & 1u)));
+                // Claims are kClaimBase + (K - 1 - rank): below every bucket
+                // word (>= -1), so the minimum over a bucket's claimants is
+                // the largest rank's, with no reset of the bucket first.
                 __syncthreads();
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
-                    if (tgt[e] >= 0) sQ[tgt[e]] = kClaimBase;
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < IPT; ++e)
-                    if (tgt[e] >= 0) atomicMax(&sQ[tgt[e]], kClaimBase + 1 + rank[e]);
+                    if (tgt[e] >= 0) atomicMin(&sQ[tgt[e]], kClaimBase + (K - 1 - rank[e]));
                 __syncthreads();
                 uint32_t lostm = 0;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
                     if (tgt[e] >= 0) {
-                        if (sQ[tgt[e]] == kClaimBase + 1 + rank[e]) {
+                        if (sQ[tgt[e]] == kClaimBase + (K - 1 - rank[e])) {
                             const int32_t word = (fp_of(uint32_t(x[e]), a.afp) << 16) | slot[e];
                             sQ[tgt[e]] = word;
                             gQ[tgt[e]] = word;  // written through, like C
