@@ -140,6 +140,9 @@ __device__ inline void map_clear_if(int32_t* mrow, int64_t map_len, int32_t id, 
     if (id >= 0 && id < map_len && map_load(mrow + id) == j) map_store(mrow + id, -1);
 }
 
+// Probe rounds issued between two early-exit checks.
+constexpr int kProbeUnroll = 4;
+
 // 0x80 in every byte of x that is zero, 0 elsewhere (exact for all values).
 __device__ inline uint32_t zero_bytes(uint32_t x) {
     return ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
@@ -373,27 +376,34 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             }
             c_visit += uint32_t(__popc(valid));
         }
-        for (int t = 0; t <= (DENSE ? -1 : R); ++t) {
+        // The wave leaves the loop once none of its ids is open, checked
+        // every kProbeUnroll rounds so that the reads of those rounds can be
+        // in flight together (bucket positions do not depend on results).
+        for (int t0 = 0; t0 <= (DENSE ? -1 : R); t0 += kProbeUnroll) {
             if (__ballot(open != 0u) == 0ull) break;
-            c_visit += uint32_t(__popc(open));
-            int32_t wd[IPT], cc[IPT];
 #pragma unroll
-            for (int e = 0; e < IPT; ++e) wd[e] = sQ[pos[e]];
+            for (int u = 0; u < kProbeUnroll; ++u) {
+                if (t0 + u > R) break;
+                c_visit += uint32_t(__popc(open));
+                int32_t wd[IPT], cc[IPT];
 #pragma unroll
-            for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
-            // Hit bits of every id first, masked by the open ids after, so
-            // that no read is moved under a branch.
-            uint32_t hitm = 0;
+                for (int e = 0; e < IPT; ++e) wd[e] = sQ[pos[e]];
 #pragma unroll
-            for (int e = 0; e < IPT; ++e)
-                hitm |= uint32_t((wd[e] != kEmpty) & (cc[e] == x[e])) << e;
-            hitm &= open;
+                for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
+                // Hit bits of every id first, masked by the open ids after,
+                // so that no read is moved under a branch.
+                uint32_t hitm = 0;
 #pragma unroll
-            for (int e = 0; e < IPT; ++e) {
-                slot[e] = ((hitm >> e) & 1u) ? (wd[e] & int32_t(smask)) : slot[e];
-                pos[e] = (pos[e] + dst[e]) & smask;
+                for (int e = 0; e < IPT; ++e)
+                    hitm |= uint32_t((wd[e] != kEmpty) & (cc[e] == x[e])) << e;
+                hitm &= open;
+#pragma unroll
+                for (int e = 0; e < IPT; ++e) {
+                    slot[e] = ((hitm >> e) & 1u) ? (wd[e] & int32_t(smask)) : slot[e];
+                    pos[e] = (pos[e] + dst[e]) & smask;
+                }
+                open &= ~hitm;
             }
-            open &= ~hitm;
         }
         // open now holds exactly the valid misses.
         const uint32_t missm = open;
@@ -607,6 +617,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                     lp[e] = home_bucket(uint32_t(x[e]), a.a1, smask);
                     ld[e] = stride_of(uint32_t(x[e]), a.a2, smask);
                 }
+                // Checked every round: most links succeed in the first.
                 uint32_t search = missm;
                 for (int t = 0; t <= R; ++t) {
                     if (__ballot(search != 0u) == 0ull) break;
