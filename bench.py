@@ -109,6 +109,12 @@ def parse():
                     help="instead of the step benchmark: threshold prefetch (ECHO) on "
                          "scored selections: the recall left on the critical path after "
                          "the exact top-K is known, with and without the prefetch")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="instead of the step benchmark: Stage-One latency of one request "
+                         "(75%% adjacent reuse) over K in 256..2048 and S in 512..8192")
+    ap.add_argument("--lifetime-sweep", action="store_true",
+                    help="instead of the step benchmark: hit rate and Stage-One latency "
+                         "of the residency shape against the lifetime L")
     ap.add_argument("--probe-sweep", action="store_true",
                     help="instead of the step benchmark: Stage-One throughput on the "
                          "residency request shape (K=2048, S=8192) at B = 32..512, "
@@ -216,6 +222,81 @@ def probe_sweep(args):
             "state_traffic_GBps": round(staged / (us * 1e-6) / 1e9, 1),
             "hit_rate": round(d[r.CNT_HITS] / d[r.CNT_LOOKUPS], 4)}), flush=True)
         rs.close()
+    return 0
+
+
+def stage1_only(r, torch, stream, w, warmup, timed, L=None, B=None):
+    """Stage One alone (no host pool) over w's steps: mean launch time from
+    events around `timed` launches after `warmup`, and the counter deltas
+    of the timed launches."""
+    cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes,
+                                L=w.L if L is None else L, R=w.R, a1=w.a1, a2=w.a2,
+                                a_fp=w.afp, flags=r.FLAG_SKIP_GATHER)
+    rs = r.RecallStep(cfg, None, w.host_rows_total, stream=stream)
+    topk = torch.from_numpy(np.ascontiguousarray(w.topk)).cuda()
+    ctx = torch.from_numpy(np.ascontiguousarray(w.ctx_len)).cuda()
+    row_base = torch.from_numpy(w.row_base).cuda()
+    host_rows = torch.from_numpy(w.host_rows).cuda()
+    ios = [rs.io(topk[t], ctx[t], row_base, host_rows) for t in range(w.steps)]
+    sh = stream.cuda_stream
+    torch.cuda.synchronize()
+    for t in range(warmup):
+        r.avsg_match(rs.handle, ios[t % w.steps], sh)
+    torch.cuda.synchronize()
+    cnt0 = rs.CNT.cpu().numpy().astype(np.int64)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(timed):
+        r.avsg_match(rs.handle, ios[(warmup + k) % w.steps], sh)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    d = (rs.CNT.cpu().numpy().astype(np.int64) - cnt0).sum(0)
+    rs.close()
+    return {"stage1_us": round(e0.elapsed_time(e1) * 1e3 / timed, 2),
+            "hit_rate": round(d[r.CNT_HITS] / max(1, d[r.CNT_LOOKUPS]), 4),
+            "lost_per_step": round((d[r.CNT_LOST_COLLISION] + d[r.CNT_LOST_EXHAUSTED]) / timed,
+                                   1),
+            "visits_per_lookup": round(d[r.CNT_PROBE_VISITS] / max(1, d[r.CNT_LOOKUPS]), 3)}
+
+
+def shape_sweep(args):
+    """Stage-One latency of one request against K and S (the in-kind
+    analog of the AVSG page's matching-latency sweep, section 4.2)."""
+    import torch
+    import recall_step_amd as r
+    from workloads.synth import gen_reuse
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    for S in (512, 1024, 2048, 4096, 8192):
+        row = {}
+        for K in (256, 512, 1024, 2048):
+            if K > S:
+                continue
+            w = gen_reuse(1, 0.75, steps=16, K=K, S=S)
+            row[str(K)] = stage1_only(r, torch, stream, w, 4, 12)
+        print(json.dumps({"shape_sweep": "one request, 75% adjacent reuse, Stage One only",
+                          "S": S, "by_K": {k: v["stage1_us"] for k, v in row.items()},
+                          "hit_rate_by_K": {k: v["hit_rate"] for k, v in row.items()}}),
+              flush=True)
+    return 0
+
+
+def lifetime_sweep(args):
+    """Hit rate and Stage-One latency of the residency shape (B=8, K=2048,
+    S=8192) against the lifetime L (the in-kind analog of the AVSG page's
+    Appendix A)."""
+    import torch
+    import recall_step_amd as r
+    from workloads import make
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    w = make("residency", steps=48, B=8)
+    for L in (1, 3, 7, 15, 63, 127):
+        res = stage1_only(r, torch, stream, w, 16, 32, L=L)
+        print(json.dumps({"lifetime_sweep": "residency shape, B=8, steps 16..47",
+                          "L": L, **res}), flush=True)
     return 0
 
 
@@ -642,6 +723,10 @@ def main():
         return 2
     if args.probe_sweep:
         return probe_sweep(args)
+    if args.shape_sweep:
+        return shape_sweep(args)
+    if args.lifetime_sweep:
+        return lifetime_sweep(args)
     if args.ratios:
         return ratios(args)
     if args.layers:
