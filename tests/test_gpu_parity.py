@@ -58,7 +58,7 @@ def test_residency_full():
 
 @pytest.mark.parametrize("K,S", [(256, 512), (1000, 1024), (2048, 2048), (3000, 4096),
                                  (4096, 8192), (1, 16), (64, 64), (1501, 2048),
-                                 (2999, 4096), (4095, 8192)])
+                                 (2999, 4096), (4095, 8192), (256, 16384), (1023, 16384)])
 def test_shape_sweep_stage_one(K, S):
     """Ragged and maximal K, several S: every IPT template, the scalar path
     for K not a multiple of the ids per thread, and every slot-per-thread
@@ -251,6 +251,24 @@ def test_state_beyond_lds_is_unsupported():
     with pytest.raises(r.AvsgError) as e:
         r.RecallStep(cfg, None, 1 << 20)
     assert e.value.code == r.AVSG_EUNSUPPORTED
+
+
+def test_largest_token_count_with_gather():
+    """B * N_q = 16384 tokens, the most the gather's prologue scans: tiny
+    requests (K = 4, S = 16) so that every token has a few misses."""
+    from workloads.synth import Workload
+    B, Nq, K, S, hr, steps = 4096, 4, 4, 16, 64, 3
+    rng = np.random.default_rng(4096)
+    topk = np.empty((steps, B, Nq, K), np.int32)
+    for t in range(steps):
+        for b in range(B):
+            for g in range(Nq):
+                topk[t, b, g] = rng.choice(hr, K, replace=False)
+    w = Workload("4096 x 4 tokens", B, Nq, K, S, 16, steps, 4096, topk,
+                 np.full((steps, B), hr, np.int32), np.full(B, hr, np.int32),
+                 np.arange(B, dtype=np.int64) * hr, L=2, R=3)
+    cnt = run_parity(w, kv_every=1)
+    assert cnt[:, 2].sum() > 0 and cnt[:, 0].sum() > 0
 
 
 def test_mtp_capacity_edge():
