@@ -20,9 +20,6 @@ constexpr size_t kStage1LdsBudget = 160 * 1024;
 constexpr int kMaxBitmapIds = 1 << 18;
 // Copies of the lifetime histogram (lane % kHistCopies picks one).
 constexpr int kHistCopies = 16;
-// Lifetime words (4 slots each) one Stage-One thread owns: S <= 16384 fits
-// the LDS budget and a workgroup has at least 256 threads.
-constexpr int kMaxLifeWords = 16;
 
 
 __host__ __device__ inline int next_pow2(int v) {

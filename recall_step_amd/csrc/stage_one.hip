@@ -9,15 +9,18 @@
 //
 // gfx950 mapping.  One workgroup owns one request for the whole step.  Its
 // bucket words and cached ids (int32) and its lifetimes are staged in LDS
-// once, every query token runs against the LDS copy, and the state is written
-// back once.  Lifetimes are held as one byte per slot, G = F + 1 (0 = dead,
+// once and every query token runs against the LDS copy.  Installs and links
+// write their C and Q entries through to global memory as they happen, so
+// the end of the step writes back only the lifetimes and the slots it
+// empties.  Lifetimes are held as one byte per slot, G = F + 1 (0 = dead,
 // L + 1 = just refreshed), so dead slots are zero bytes.
 //
 // A workgroup has 256 to 1024 threads, two ids per thread by default (up to
-// eight): the probe and link rounds are bound by LDS latency, which more
-// waves hide, while the fixed per-thread work (scans, reductions, barriers)
-// grows with the wave count; DPP scans and one-barrier workgroup reductions
-// keep that part small.
+// eight).  The probe and link rounds wait on LDS, which more waves hide, but
+// with four waves per SIMD every per-thread instruction is issued four times
+// over, so the code keeps instruction counts low: branch-free rounds (every
+// read from an always-valid index, results masked afterwards), DPP scans,
+// one-barrier workgroup reductions, counters from ballots.
 //
 // Each thread owns IPT consecutive positions of a token's top-K list and
 // carries their ids through the whole token: it probes them, refreshes its
@@ -33,9 +36,10 @@
 // Victims: the dead-slot count is an exclusive scan over slots in index
 // order; only when it is short of the miss count does the workgroup build a
 // lifetime histogram (16 LDS copies to spread atomics) to find the least
-// extra decay.  Contested buckets are resolved with an LDS atomicMax on the
-// miss rank, so no result depends on wave scheduling.  Wave scans use DPP
-// row shifts and row broadcasts; a workgroup scan needs one barrier.
+// extra decay.  Contested buckets are resolved with an LDS atomicMin on
+// claims encoded below every bucket word (the largest miss rank wins), so no
+// result depends on wave scheduling.  Wave scans use DPP row shifts and row
+// broadcasts; a workgroup scan needs one barrier.
 #include "internal.h"
 
 namespace avsg {
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     // This thread's contiguous run of lifetime words (4 slots each) for the
     // S-wide passes.
     const int nd = S >> 2;
-    const int D = nd >= T ? nd / T : 1;  // <= kMaxLifeWords (S <= 16384, T >= 256)
+    const int D = nd >= T ? nd / T : 1;  // <= 16: S <= 16384 fits LDS, T >= 256
     const int dw0 = tid * D;
     const int dwn = dw0 < nd ? D : 0;
 
