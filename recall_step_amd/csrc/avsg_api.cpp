@@ -177,8 +177,7 @@ int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs, avsg_handle** 
     h->host_dev = host_dev;
     h->device = dev;
     h->lds_bytes = lds;
-    h->gather_blocks = cfg->gather_blocks > 0 ? cfg->gather_blocks
-                                              : 2 * prop.multiProcessorCount;
+    h->gather_blocks = cfg->gather_blocks > 0 ? cfg->gather_blocks : prop.multiProcessorCount;
     h->stage1_threads = avsg::stage1_threads(cfg->K, cfg->stage1_threads);
     e = hipMalloc(reinterpret_cast<void**>(&h->ws_pairs), avsg_workspace_bytes(cfg));
     if (e != hipSuccess) {

@@ -13,9 +13,11 @@
 // copies flat misses [w*M/G, (w+1)*M/G).  Rows are resolved 256 at a time into
 // LDS (source and destination byte offsets), after which consecutive lanes
 // move consecutive 16-byte chunks of a row: one wave reads 1 KiB of a row's
-// contiguous host bytes per instruction, and each lane keeps several loads in
-// flight before storing.  A grid of twice the CU count measured best on
-// gfx950: the host link is saturated with fewer requests queued.
+// contiguous host bytes per instruction, and each lane keeps two loads in
+// flight before storing.  One workgroup per CU, two loads per lane (about
+// 2 MiB in flight) measured best on gfx950: the host link is saturated well
+// before that, and more requests in flight (twice the grid, or four or
+// eight loads per lane) made the same copy 2-15 % slower.
 //
 // The two partitions the page compares against share the copy loop: by
 // request (workgroup w copies all misses of requests w, w+G, ...) and by
@@ -28,7 +30,7 @@ namespace avsg {
 namespace {
 
 constexpr int T = kGatherThreads;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;
 
 __device__ inline int wave_incl_scan(int v) {
     const int lane = __lane_id();
@@ -74,7 +76,9 @@ __device__ inline void row_offsets(const GatherArgs& a, int bq, int32_t x, int32
 // Copy nrows rows whose byte offsets are in LDS.  The loads of an iteration
 // are unconditional (a rejected row reads row 0 of the pool, always in
 // bounds) so all kUnroll are in flight at once; only the stores are
-// predicated.  Ends with a barrier so the offsets may be rewritten.
+// predicated.  No barrier at the end (a workgroup's last pass then retires
+// without waiting for its stores): a caller that rewrites the offsets
+// afterwards puts a barrier first.
 __device__ inline void copy_rows(const GatherArgs& a, const int64_t* sSrc, const int64_t* sDst,
                                  int nrows) {
     const int cpr = a.row_bytes >> 4;  // 16-byte chunks per row
@@ -97,7 +101,6 @@ __device__ inline void copy_rows(const GatherArgs& a, const int64_t* sSrc, const
         for (int u = 0; u < kUnroll; ++u)
             if (d[u] >= 0) *reinterpret_cast<int4*>(a.dev + d[u]) = v[u];
     }
-    __syncthreads();
 }
 
 __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
@@ -146,6 +149,7 @@ __global__ __launch_bounds__(T) void gather_kernel(GatherArgs a) {
         }
         __syncthreads();
         copy_rows(a, sSrc, sDst, nrows);
+        if (base + kGatherRowsPerPass < hi) __syncthreads();  // offsets rewritten next
     }
 }
 
@@ -167,6 +171,7 @@ __global__ __launch_bounds__(T) void gather_by_request_kernel(GatherArgs a) {
                 }
                 __syncthreads();
                 copy_rows(a, sSrc, sDst, nrows);
+                __syncthreads();
             }
         }
     }
@@ -200,6 +205,8 @@ __global__ __launch_bounds__(T) void gather_by_topk_kernel(GatherArgs a) {
             const int off = block_excl_scan(miss ? 1 : 0, sWave, &tot);
             if (miss) row_offsets(a, bq, a.topk[e], a.slot_table[e], &sSrc[off], &sDst[off]);
             __syncthreads();
+            // The next range's scan starts with a barrier, so its offsets
+            // are written only after this copy has read them.
             if (tot > 0) copy_rows(a, sSrc, sDst, tot);
         }
     }
