@@ -1,0 +1,46 @@
+"""The bench's host-side contract (no GPU needed): it refuses more than one
+GPU with a message, reports the profiled gather traffic only for the gather
+sources the profile was taken on, and prices Stage One's algorithmic bytes
+by the unit costs it documents."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_profiled_traffic_follows_the_gather_sources(tmp_path, monkeypatch):
+    # The committed summary matches the committed sources.
+    assert bench.profiled_traffic("matching") is not None
+    assert bench.profiled_traffic("residency") is None
+    # Any change to the gather's sources makes the figure stale.
+    src = tmp_path / "gather.hip"
+    src.write_bytes(open(bench.GATHER_SOURCES[0], "rb").read() + b"\n// changed\n")
+    monkeypatch.setattr(bench, "GATHER_SOURCES", [str(src), bench.GATHER_SOURCES[1]])
+    assert bench.profiled_traffic("matching") is None
+
+
+@pytest.mark.parametrize("B,S,Nq,lookups,visits,misses", [(1, 16, 1, 0, 0, 0),
+                                                          (8, 2048, 1, 16384, 40000, 11000),
+                                                          (3, 64, 4, 30, 70, 9)])
+def test_stage_one_algorithmic_bytes(B, S, Nq, lookups, visits, misses):
+    expect = (B * 2 * S * 4          # lifetimes read and written once per request
+              + lookups * (4 + 4 + 1)  # id in, slot out, mask out
+              + visits * 8           # bucket word and cached id per visit
+              + misses * (12 + 8)    # install (C, F, Q) and miss-list entry
+              + B * Nq * 4)          # miss count per token
+    assert bench.stage1_algorithmic_bytes(B, S, Nq, lookups, visits, misses) == expect
