@@ -90,6 +90,20 @@ __device__ inline int block_excl_scan(int v, int32_t* scr, int* total) {
     return incl - v + pre;
 }
 
+// Workgroup sum of v.  One barrier; scr holds kMaxWaves ints.
+template <int T>
+__device__ inline int block_sum(int v, int32_t* scr) {
+    constexpr int NW = T / 64;
+    const int w = threadIdx.x >> 6;
+    v = lane63(wave_scan_add(v));
+    if (__lane_id() == 0) scr[w] = v;
+    __syncthreads();
+    int s = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) s += scr[u];
+    return s;
+}
+
 // Workgroup sum of v, min of lo and max of hi.  One barrier; scr holds
 // 3 * kMaxWaves ints.
 template <int T>
@@ -316,6 +330,8 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     const int32_t hr = a.host_rows[b];
     const bool row_ok = rb >= 0 && hr >= 0 && rb + hr <= a.host_rows_total;
     const int32_t N = a.ctx_len[b];
+    // The rank bitmap can cover all of the request's ids.
+    const bool narrow_rows = row_ok && hr > 0 && hr <= lay.bitmap_words * 32;
 
     // This thread's contiguous run of lifetime words (4 slots each) for the
     // S-wide passes.
@@ -423,10 +439,19 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         }
         const int m_local = __popc(missm);
 
-        // Miss and valid-id totals in one sum (each at most K < 2^16).
+        // Miss and valid-id totals in one sum (each at most K < 2^16).  When
+        // the request's rows fit the rank bitmap, the bitmap spans [0,
+        // host_rows) (every valid id is below it) and the id range is not
+        // reduced.
         int nsum, idlo, idhi;
-        block_sum_min_max<T>(m_local | (__popc(valid) << 16), lo_local, hi_local, sMM, &nsum,
-                             &idlo, &idhi);
+        if (narrow_rows) {
+            nsum = block_sum<T>(m_local | (__popc(valid) << 16), sMM);
+            idlo = 0;
+            idhi = hr - 1;
+        } else {
+            block_sum_min_max<T>(m_local | (__popc(valid) << 16), lo_local, hi_local, sMM, &nsum,
+                                 &idlo, &idhi);
+        }
         const int ng = min(nsum & 0xFFFF, K);
         const int nvalid = nsum >> 16;
         c_look += uint32_t(nvalid);
