@@ -271,6 +271,36 @@ def test_largest_token_count_with_gather():
     assert cnt[:, 2].sum() > 0 and cnt[:, 0].sum() > 0
 
 
+def test_edge_inputs_of_each_request():
+    """Requests whose inputs sit at the edges the method leaves to the
+    caller, side by side in one batch: rows leaving the pool, a negative row
+    base, no host rows, a verified length of 0, below 0 and beyond the rows,
+    and an all-padding token.  Ids outside a request's valid rows are
+    padding with the error bit, and invalidation follows N as given."""
+    from workloads.synth import Workload
+    B, Nq, K, S, steps = 8, 2, 8, 32, 6
+    rb = np.array([0, 64, 250, 64, 128, 192, -5, 240], np.int64)
+    hr = np.array([64, 0, 16, 64, 64, 64, 16, 16], np.int32)  # pool: 256 rows
+    n_of = [64, 10, 16, 0, -3, 1000, 8, 8]
+    rng = np.random.default_rng(99)
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    ctx = np.zeros((steps, B), np.int32)
+    for t in range(steps):
+        for b in range(B):
+            ctx[t, b] = n_of[b]
+            for g in range(Nq):
+                if b == 0 and g == 1 and t % 2:
+                    continue  # an all-padding token
+                n = min(K, max(int(hr[b]), 1))
+                topk[t, b, g, :n] = rng.choice(max(int(hr[b]), 16), n, replace=False)
+    w = Workload("edge inputs", B, Nq, K, S, 64, steps, 99, topk, ctx, hr, rb, L=2, R=3)
+    assert w.host_rows_total == 256
+    cnt = run_parity(w, kv_every=1)
+    assert (cnt[[1, 2, 6], 6] & 1).all()           # no rows, off the pool, negative base
+    assert (cnt[[1, 2, 6], 0] == 0).all() and (cnt[[1, 2, 6], 2] == 0).all()
+    assert cnt[[0, 3, 4, 5, 7], 2].min() > 0
+
+
 def test_mtp_capacity_edge():
     """N_q * K == S with L = 1: the extra decay reaches its bound every token."""
     w = make("mtp3", steps=4, B=2)
