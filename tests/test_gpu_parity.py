@@ -388,6 +388,63 @@ def test_hip_graph_capture_and_replay():
         p.close()
 
 
+def test_dense_map_in_a_captured_graph():
+    """The dense matcher's step (map reads, clears and atomic maxima) replays
+    from a captured graph to the oracle's results, map included."""
+    import torch
+    import recall_step_amd as r
+    w = make("residency", steps=6, B=4)
+    say("[parity] graph capture residency B=4 dense")
+    p = Pair(w, flags=r.FLAG_DENSE_MAP)
+    try:
+        dev = p.rs.Q.device
+        topk_in = torch.empty_like(p.topk[0])
+        ctx_in = torch.empty_like(p.ctx[0])
+        io = p.rs.io(topk_in, ctx_in, p.row_base, p.host_rows)
+        topk_in.copy_(p.topk[0])
+        ctx_in.copy_(p.ctx[0])
+        p.rs.step(io)
+        p.compare(p.oracle_step(0), "dense graph eager step 0")
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                p.rs.step(io, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        for t in range(1, w.steps):
+            topk_in.copy_(p.topk[t])
+            ctx_in.copy_(p.ctx[t])
+            g.replay()
+            torch.cuda.synchronize()
+            p.compare(p.oracle_step(t), f"dense graph replay step {t}", check_kv=True)
+    finally:
+        p.close()
+
+
+def test_two_handles_on_two_streams_concurrently():
+    """Two handles stepped on two streams at once, each against its own
+    oracle: the library keeps no state between handles."""
+    import torch
+    say("[parity] two handles, two streams")
+    pa = Pair(make("matching", steps=6))
+    pb = Pair(make("residency", steps=6, B=4))
+    try:
+        sa = torch.cuda.Stream(device=pa.rs.Q.device)
+        sb = torch.cuda.Stream(device=pb.rs.Q.device)
+        sa.wait_stream(torch.cuda.current_stream())
+        sb.wait_stream(torch.cuda.current_stream())
+        for t in range(6):
+            pa.rs.step(pa.io(t), stream=sa)
+            pb.rs.step(pb.io(t), stream=sb)
+            torch.cuda.synchronize()
+            pa.compare(pa.oracle_step(t), f"stream A step {t}", check_kv=t == 5)
+            pb.compare(pb.oracle_step(t), f"stream B step {t}", check_kv=t == 5)
+    finally:
+        pa.close()
+        pb.close()
+
+
 def test_determinism_repeat_from_same_state():
     import torch
     w = make("matching", steps=3)
