@@ -121,3 +121,44 @@ def test_product_does_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(root, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_header_compiles_as_c99_and_links(tmp_path):
+    """A plain C program includes the header, links the library and calls
+    the entry points that need no GPU: the ABI is C, not C++."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(r._LIB_PATH)
+    src = tmp_path / "use_avsg.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "avsg.h"
+int main(void) {
+    avsg_config c;
+    avsg_buffers bufs = {0};
+    avsg_handle* h = (avsg_handle*)1;
+    if (avsg_version() != AVSG_VERSION) return 1;
+    avsg_config_default(&c, 8, 1, 2048, 2048, 1280);
+    if (avsg_validate_config(&c) != AVSG_OK) return 2;
+    if (avsg_stage1_lds_bytes(&c) == 0 || avsg_workspace_bytes(&c) != 8u * 2048u * 8u) return 3;
+    c.S = 3000;
+    if (avsg_validate_config(&c) != AVSG_EINVAL) return 4;
+    if (avsg_create(&c, &bufs, &h) != AVSG_EINVAL || h != NULL) return 5;
+    if (avsg_destroy(NULL) != AVSG_OK) return 6;
+    printf("%s\n", avsg_strerror(AVSG_EUNSUPPORTED));
+    return 0;
+}
+""")
+    exe = tmp_path / "use_avsg"
+    cmd = [cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(root, "include"), str(src), "-o", str(exe),
+           "-L", lib_dir, "-lavsg", f"-Wl,-rpath,{lib_dir}"]
+    b = subprocess.run(cmd, capture_output=True, text=True)
+    assert b.returncode == 0, b.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stderr)
+    assert "beyond this build" in run.stdout
