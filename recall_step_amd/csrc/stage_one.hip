@@ -405,9 +405,12 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             for (int u = 0; u < kProbeUnroll; ++u) {
                 if (t0 + u > R) break;
                 c_visit += uint32_t(__popc(open));
+                // Closed ids read bucket 0 (and so the slot its word names):
+                // one address shared by many lanes is a broadcast, not a
+                // bank conflict, and the round stays branch-free.
                 int32_t wd[IPT], cc[IPT];
 #pragma unroll
-                for (int e = 0; e < IPT; ++e) wd[e] = sQ[pos[e]];
+                for (int e = 0; e < IPT; ++e) wd[e] = sQ[((open >> e) & 1u) ? pos[e] : 0u];
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
                 // Hit bits of every id first, masked by the open ids after,
@@ -652,7 +655,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                     if (__ballot(search != 0u) == 0ull) break;
                     int32_t wd[IPT], cc[IPT];
 #pragma unroll
-                    for (int e = 0; e < IPT; ++e) wd[e] = sQ[lp[e]];
+                    for (int e = 0; e < IPT; ++e) wd[e] = sQ[((search >> e) & 1u) ? lp[e] : 0u];
 #pragma unroll
                     for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
                     uint32_t takem = 0;
