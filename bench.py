@@ -119,7 +119,10 @@ def parse():
                     help="instead of the step benchmark: Stage-One throughput on the "
                          "residency request shape (K=2048, S=8192) at B = 32..512, "
                          "one JSON line per batch size")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
+    return args
 
 
 def hip_runtime():

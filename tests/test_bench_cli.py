@@ -44,3 +44,9 @@ def test_stage_one_algorithmic_bytes(B, S, Nq, lookups, visits, misses):
               + misses * (12 + 8)    # install (C, F, Q) and miss-list entry
               + B * Nq * 4)          # miss count per token
     assert bench.stage1_algorithmic_bytes(B, S, Nq, lookups, visits, misses) == expect
+
+
+def test_step_counts_are_validated():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--steps" in r.stderr
