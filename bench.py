@@ -743,7 +743,15 @@ def main():
     from workloads import make
 
     torch.cuda.set_device(0)
+    # Enough distinct steps for the warm-up and the timed steps, so that no
+    # selection is replayed onto a buffer that already holds it.  The MTP-3
+    # workload is defined as 32 iterations (its verified length grows into
+    # the end of the host rows), so it is replayed from its start if more
+    # steps are asked for.
+    need = args.warmup + args.steps
     w = make(args.workload)
+    if args.workload != "mtp3" and need > w.steps:
+        w = make(args.workload, steps=need)
     log(f"[bench] workload {w.name}: B={w.B} Nq={w.Nq} K={w.K} S={w.S} "
         f"row={w.row_bytes} host_bytes={w.host_bytes} steps={args.steps} warmup={args.warmup}")
     stream = torch.cuda.Stream()
