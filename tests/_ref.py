@@ -8,8 +8,8 @@ structured differently from the oracle on purpose, and only fit tiny inputs.
   * the Probe primitive examines *every* one of the R+1 buckets (section 3.3)
     and the smallest matching round is taken afterwards;
   * the hash is evaluated in exact integer arithmetic, ``(a1*x) % S``;
-  * "decaying all records further until enough die" (section 3.3) is run as
-    repeated unit decays rather than a computed amount;
+  * the extra decay of section 3.3, which continues until enough records have
+    died, is run as repeated unit decays rather than a computed amount;
   * every reusable round of the link probe is listed, then the first taken;
     contested buckets are resolved by grouping claims per bucket (App. B,
     "Collision and probe-budget semantics").
