@@ -69,6 +69,18 @@ __device__ inline int wave_scan_min(int x) { AVSG_DPP_SCAN(x, op_min, INT32_MAX)
 __device__ inline int wave_scan_max(int x) { AVSG_DPP_SCAN(x, op_max, INT32_MIN); return x; }
 __device__ inline int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
 
+// Inclusive scans within each row of 16 lanes.
+#define AVSG_DPP_ROW_SCAN(x, OP, ID)                                              \
+    do {                                                                          \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x111, 0xf, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x112, 0xf, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x114, 0xf, 0xf, false));    \
+        x = OP(x, __builtin_amdgcn_update_dpp(ID, x, 0x118, 0xf, 0xf, false));    \
+    } while (0)
+__device__ inline int row_scan_add(int x) { AVSG_DPP_ROW_SCAN(x, op_add, 0); return x; }
+__device__ inline int row_scan_min(int x) { AVSG_DPP_ROW_SCAN(x, op_min, INT32_MAX); return x; }
+__device__ inline int row_scan_max(int x) { AVSG_DPP_ROW_SCAN(x, op_max, INT32_MIN); return x; }
+
 // Exclusive scan of one int per thread over the workgroup; *total gets the
 // sum.  One barrier.  scr holds kMaxWaves ints; two consecutive workgroup
 // operations must use different scratch buffers.
@@ -79,14 +91,12 @@ __device__ inline int block_excl_scan(int v, int32_t* scr, int* total) {
     const int incl = wave_scan_add(v);
     if (__lane_id() == 63) scr[w] = incl;
     __syncthreads();
-    int pre = 0, tot = 0;
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-        const int s = scr[u];
-        pre += u < w ? s : 0;
-        tot += s;
-    }
-    *total = tot;
+    // Lanes 0..NW-1 (NW <= 16: one DPP row) scan the wave totals; each wave
+    // reads its prefix with one readlane.
+    const int s = row_scan_add(__lane_id() < NW ? scr[__lane_id()] : 0);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int pre = wu > 0 ? __builtin_amdgcn_readlane(s, wu - 1) : 0;
+    *total = __builtin_amdgcn_readlane(s, NW - 1);
     return incl - v + pre;
 }
 
@@ -98,10 +108,8 @@ __device__ inline int block_sum(int v, int32_t* scr) {
     v = lane63(wave_scan_add(v));
     if (__lane_id() == 0) scr[w] = v;
     __syncthreads();
-    int s = 0;
-#pragma unroll
-    for (int u = 0; u < NW; ++u) s += scr[u];
-    return s;
+    return __builtin_amdgcn_readlane(row_scan_add(__lane_id() < NW ? scr[__lane_id()] : 0),
+                                     NW - 1);
 }
 
 // Workgroup sum of v, min of lo and max of hi.  One barrier; scr holds
@@ -120,16 +128,11 @@ __device__ inline void block_sum_min_max(int v, int lo, int hi, int32_t* scr, in
         scr[2 * kMaxWaves + w] = hi;
     }
     __syncthreads();
-    int s = 0, a = INT32_MAX, c = INT32_MIN;
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-        s += scr[u];
-        a = min(a, scr[kMaxWaves + u]);
-        c = max(c, scr[2 * kMaxWaves + u]);
-    }
-    *sum = s;
-    *mn = a;
-    *mx = c;
+    const int l = __lane_id();
+    const bool in = l < NW;
+    *sum = __builtin_amdgcn_readlane(row_scan_add(in ? scr[l] : 0), NW - 1);
+    *mn = __builtin_amdgcn_readlane(row_scan_min(in ? scr[kMaxWaves + l] : INT32_MAX), NW - 1);
+    *mx = __builtin_amdgcn_readlane(row_scan_max(in ? scr[2 * kMaxWaves + l] : INT32_MIN), NW - 1);
 }
 
 __device__ inline uint32_t home_bucket(uint32_t x, uint32_t a1, uint32_t smask) {
