@@ -248,6 +248,37 @@ __device__ inline void store_outputs(int32_t* __restrict__ O, int8_t* __restrict
     }
 }
 
+// Stage nq int4 words of Q, C and F into LDS, U words per thread per pass.
+// Branch-free so that all loads of a pass are in flight together: indices
+// past the end are clamped to the last word, and the threads that clamp
+// store that word's own value again.
+template <int T, int U, bool DENSE>
+__device__ inline void stage_words(const int32_t* gQ, const int32_t* gC, const int32_t* gF,
+                                   int32_t* sQ, int32_t* sC, uint32_t* sGw, int nq, int gadd,
+                                   int L) {
+    for (int j0 = threadIdx.x; j0 < nq; j0 += U * T) {
+        int4 q[U], c[U], f[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(j0 + u * T, nq - 1);
+            if constexpr (!DENSE) q[u] = reinterpret_cast<const int4*>(gQ)[j];
+            c[u] = reinterpret_cast<const int4*>(gC)[j];
+            f[u] = reinterpret_cast<const int4*>(gF)[j];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(j0 + u * T, nq - 1);
+            if constexpr (!DENSE) reinterpret_cast<int4*>(sQ)[j] = q[u];
+            reinterpret_cast<int4*>(sC)[j] = c[u];
+            const uint32_t g0 = uint32_t(min(max(f[u].x + gadd, 0), L + 1));
+            const uint32_t g1 = uint32_t(min(max(f[u].y + gadd, 0), L + 1));
+            const uint32_t g2 = uint32_t(min(max(f[u].z + gadd, 0), L + 1));
+            const uint32_t g3 = uint32_t(min(max(f[u].w + gadd, 0), L + 1));
+            sGw[j] = g0 | (g1 << 8) | (g2 << 16) | (g3 << 24);
+        }
+    }
+}
+
 // DENSE: the dense id -> slot matcher.  A valid id (also below map_len) is
 // a hit iff its map entry m is a slot in [0, S) that caches it; installs
 // drop the victim's old entry if it still points at the victim, clear every
@@ -292,11 +323,11 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                      (reinterpret_cast<uintptr_t>(a.hit_mask) % IPT) == 0;
     const int i0 = tid * IPT;
 
-    // First token's ids and the counters are fetched while the state is
-    // staged.
-    int32_t xn[IPT];
-    load_ids<IPT>(a.topk + size_t(b) * a.Nq * K, i0, K, vec, xn);
-    const int32_t cnt_old = tid < 8 ? a.CNT[size_t(b) * 8 + tid] : 0;
+    // The request's scalars are read before anything else so that their
+    // latency overlaps the staging loads.
+    const int64_t rb = a.row_base[b];
+    const int32_t hr = a.host_rows[b];
+    const int32_t N = a.ctx_len[b];
     int32_t* const mrow = DENSE ? a.map + size_t(b) * size_t(a.map_len) : nullptr;
 
     // Stage the request's state.  The once-per-step decay before the first
@@ -304,35 +335,21 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     // [0, L + 1] for any input.  A continuation of the step (more query
     // tokens after an earlier call) stages G = F + 1 without the decay.
     const int gadd = a.predecay ? 0 : 1;
-    for (int j0 = tid; j0 < (S >> 2); j0 += 4 * T) {
-        // Loads clamped to the last word (always in bounds), stores guarded.
-        int4 q[4], c[4], f[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = min(j0 + u * T, (S >> 2) - 1);
-            if constexpr (!DENSE) q[u] = reinterpret_cast<const int4*>(gQ)[j];
-            c[u] = reinterpret_cast<const int4*>(gC)[j];
-            f[u] = reinterpret_cast<const int4*>(gF)[j];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = j0 + u * T;
-            if (j < (S >> 2)) {
-                if constexpr (!DENSE) reinterpret_cast<int4*>(sQ)[j] = q[u];
-                reinterpret_cast<int4*>(sC)[j] = c[u];
-                const uint32_t g0 = uint32_t(min(max(f[u].x + gadd, 0), L + 1));
-                const uint32_t g1 = uint32_t(min(max(f[u].y + gadd, 0), L + 1));
-                const uint32_t g2 = uint32_t(min(max(f[u].z + gadd, 0), L + 1));
-                const uint32_t g3 = uint32_t(min(max(f[u].w + gadd, 0), L + 1));
-                sGw[j] = g0 | (g1 << 8) | (g2 << 16) | (g3 << 24);
-            }
-        }
-    }
+    const int nq = S >> 2;  // int4 words per array
+    if (nq <= T)
+        stage_words<T, 1, DENSE>(gQ, gC, gF, sQ, sC, sGw, nq, gadd, L);
+    else if (nq <= 2 * T)
+        stage_words<T, 2, DENSE>(gQ, gC, gF, sQ, sC, sGw, nq, gadd, L);
+    else
+        stage_words<T, 4, DENSE>(gQ, gC, gF, sQ, sC, sGw, nq, gadd, L);
+    // The first token's ids and the counters are loaded after the state's
+    // loads are issued: loads pending when the staging loop starts would be
+    // waited for at its head, before any state load.
+    int32_t xn[IPT];
+    load_ids<IPT>(a.topk + size_t(b) * a.Nq * K, i0, K, vec, xn);
+    const int32_t cnt_old = tid < 8 ? a.CNT[size_t(b) * 8 + tid] : 0;
 
-    const int64_t rb = a.row_base[b];
-    const int32_t hr = a.host_rows[b];
     const bool row_ok = rb >= 0 && hr >= 0 && rb + hr <= a.host_rows_total;
-    const int32_t N = a.ctx_len[b];
     // The rank bitmap can cover all of the request's ids.
     const bool narrow_rows = row_ok && hr > 0 && hr <= lay.bitmap_words * 32;
 
