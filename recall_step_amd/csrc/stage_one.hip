@@ -369,7 +369,10 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
 
     __syncthreads();
 
-    for (int g = 0; g < a.Nq; ++g) {
+    // N_q >= 1: a do-while leaves no path on which the loop body is skipped,
+    // so no load issued before it can still be pending after it.
+    int g = 0;
+    do {
         const size_t tok = size_t(b) * a.Nq + g;
         int32_t* O = a.slot_table + tok * K;
         int8_t* H = a.hit_mask + tok * K;
@@ -448,6 +451,11 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 open &= ~hitm;
             }
         }
+        // The next token's ids are consumed here, before this token issues
+        // any store: waiting for a load still in flight at the token's end
+        // would also wait for all of the token's stores.
+#pragma unroll
+        for (int e = 0; e < IPT; ++e) asm volatile("" ::"v"(xn[e]));
         // open now holds exactly the valid misses.
         const uint32_t missm = open;
         int lo_local = INT32_MAX, hi_local = INT32_MIN;
@@ -738,7 +746,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         store_outputs<IPT>(O, H, i0, K, vec, o, hm);
         if (tid == 0) a.n_miss[tok] = ng;
         __syncthreads();
-    }
+    } while (++g < a.Nq);
 
     // End of step: empty every slot caching a speculative id (>= N) and
     // write the lifetimes back (F = G - 1).  Installs and links wrote C and Q
