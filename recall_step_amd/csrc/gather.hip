@@ -13,11 +13,11 @@
 // copies flat misses [w*M/G, (w+1)*M/G).  Rows are resolved 256 at a time into
 // LDS (source and destination byte offsets), after which consecutive lanes
 // move consecutive 16-byte chunks of a row: one wave reads 1 KiB of a row's
-// contiguous host bytes per instruction, and each lane keeps two loads in
-// flight before storing.  One workgroup per CU, two loads per lane (about
-// 2 MiB in flight) measured best on gfx950: the host link is saturated well
-// before that, and more requests in flight (twice the grid, or four or
-// eight loads per lane) made the same copy 2-15 % slower.
+// contiguous host bytes per instruction.  One workgroup per CU and one
+// 16-byte load per lane (about 1 MiB in flight) measured best on gfx950: the
+// host link is saturated well before that, and more requests in flight (two,
+// four or eight loads per lane, or twice the grid) made the same copy 1-15 %
+// slower.
 //
 // The two partitions the page compares against share the copy loop: by
 // request (workgroup w copies all misses of requests w, w+G, ...) and by
@@ -30,7 +30,7 @@ namespace avsg {
 namespace {
 
 constexpr int T = kGatherThreads;
-constexpr int kUnroll = 2;
+constexpr int kUnroll = 1;
 
 __device__ inline int wave_incl_scan(int v) {
     const int lane = __lane_id();
@@ -73,10 +73,14 @@ __device__ inline void row_offsets(const GatherArgs& a, int bq, int32_t x, int32
     *dst = (int64_t(bq) * a.S + v) * int64_t(a.row_bytes);
 }
 
-// Copy nrows rows whose byte offsets are in LDS.  The loads of an iteration
-// are unconditional (a rejected row reads row 0 of the pool, always in
-// bounds) so all kUnroll are in flight at once; only the stores are
-// predicated.  No barrier at the end (a workgroup's last pass then retires
+// A native 16-byte vector: an array of HIP's int4 (a struct around a union)
+// can be left in scratch memory, where each load is waited for on its own.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Copy nrows rows whose byte offsets are in LDS, kUnroll 16-byte chunks per
+// lane and pass.  The loads of a pass are unconditional (a rejected row
+// reads row 0 of the pool, always in bounds) so all of them are in flight
+// at once; only the stores are predicated.  No barrier at the end (a workgroup's last pass then retires
 // without waiting for its stores): a caller that rewrites the offsets
 // afterwards puts a barrier first.
 __device__ inline void copy_rows(const GatherArgs& a, const int64_t* sSrc, const int64_t* sDst,
@@ -84,7 +88,7 @@ __device__ inline void copy_rows(const GatherArgs& a, const int64_t* sSrc, const
     const int cpr = a.row_bytes >> 4;  // 16-byte chunks per row
     const int items = nrows * cpr;
     for (int it0 = threadIdx.x; it0 < items; it0 += T * kUnroll) {
-        int4 v[kUnroll];
+        i32x4 v[kUnroll];
         int64_t d[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -93,13 +97,13 @@ __device__ inline void copy_rows(const GatherArgs& a, const int64_t* sSrc, const
             const int row = itc / cpr;
             const int c = itc - row * cpr;
             const int64_t src = sSrc[row];
-            v[u] = *reinterpret_cast<const int4*>(a.host + max(src, int64_t(0)) +
-                                                  int64_t(c) * 16);
+            v[u] = *reinterpret_cast<const i32x4*>(a.host + max(src, int64_t(0)) +
+                                                   int64_t(c) * 16);
             d[u] = (it < items && src >= 0) ? sDst[row] + int64_t(c) * 16 : int64_t(-1);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            if (d[u] >= 0) *reinterpret_cast<int4*>(a.dev + d[u]) = v[u];
+            if (d[u] >= 0) *reinterpret_cast<i32x4*>(a.dev + d[u]) = v[u];
     }
 }
 
