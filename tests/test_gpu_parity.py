@@ -56,6 +56,16 @@ def test_residency_full():
     run_parity(make("residency"), kv_every=32)
 
 
+def test_more_requests_than_cus_at_the_largest_state():
+    """300 requests of the residency shape (S = 8192: 132.5 KiB of LDS, one
+    workgroup per CU), more workgroups than the 256 CUs, so they run in two
+    rounds.  24 steps, so that the slot buffers fill and victims need the
+    extra decay.  Stage One only: the host pool of 300 such requests would
+    not fit host memory."""
+    cnt = run_parity(make("residency", steps=24, B=300), gather=False, label="residency B=300")
+    assert cnt[:, 5].sum() > 0  # live evictions: the buffers did fill
+
+
 @pytest.mark.parametrize("K,S", [(256, 512), (1000, 1024), (2048, 2048), (3000, 4096),
                                  (4096, 8192), (1, 16), (64, 64), (1501, 2048),
                                  (2999, 4096), (4095, 8192), (256, 16384), (1023, 16384)])
