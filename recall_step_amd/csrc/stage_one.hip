@@ -665,20 +665,37 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                     if (missm & (1u << e))
                         __hip_atomic_fetch_max(mrow + x[e], slot[e], __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
+                // Miss list (id, slot) in rank order.
+                int2* P = reinterpret_cast<int2*>(a.pairs) + tok * K;
+                for (int r = tid; r < ng; r += T) P[r] = sPair[r];
             } else {
                 // --- Link: first reusable bucket in R+1 rounds, judged on the
                 // bucket words before this token's writes and the slots after its
                 // installs; one scatter, the largest rank keeps a contested bucket.
-                int32_t tgt[IPT];
+                // Thread tid links the misses of rank tid + e*T, read from the
+                // rank-ordered pairs: the ng misses fill the first waves one per
+                // lane and the other waves leave at the first round, where a
+                // link by the owning thread keeps every wave walking the rounds.
+                int32_t lx[IPT], ls[IPT], tgt[IPT];
                 uint32_t lp[IPT], ld[IPT];
+                uint32_t search = 0;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
+                    const int r = tid + e * T;
+                    const int2 pr = r < ng ? sPair[r] : make_int2(0, 0);
+                    lx[e] = pr.x;
+                    ls[e] = pr.y;
+                    search |= uint32_t(r < ng) << e;
                     tgt[e] = -1;
-                    lp[e] = home_bucket(uint32_t(x[e]), a.a1, smask);
-                    ld[e] = stride_of(uint32_t(x[e]), a.a2, smask);
+                    lp[e] = home_bucket(uint32_t(lx[e]), a.a1, smask);
+                    ld[e] = stride_of(uint32_t(lx[e]), a.a2, smask);
                 }
+                // Miss list (id, slot) in rank order, from the same registers.
+                int2* P = reinterpret_cast<int2*>(a.pairs) + tok * K;
+#pragma unroll
+                for (int e = 0; e < IPT; ++e)
+                    if ((search >> e) & 1u) P[tid + e * T] = make_int2(lx[e], ls[e]);
                 // Checked every round: most links succeed in the first.
-                uint32_t search = missm;
                 for (int t = 0; t <= R; ++t) {
                     if (__ballot(search != 0u) == 0ull) break;
                     int32_t wd[IPT], cc[IPT];
@@ -709,14 +726,14 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 __syncthreads();
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
-                    if (tgt[e] >= 0) atomicMin(&sQ[tgt[e]], kClaimBase + (K - 1 - rank[e]));
+                    if (tgt[e] >= 0) atomicMin(&sQ[tgt[e]], kClaimBase + (K - 1 - (tid + e * T)));
                 __syncthreads();
                 uint32_t lostm = 0;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
                     if (tgt[e] >= 0) {
-                        if (sQ[tgt[e]] == kClaimBase + (K - 1 - rank[e])) {
-                            const int32_t word = (fp_of(uint32_t(x[e]), a.afp) << 16) | slot[e];
+                        if (sQ[tgt[e]] == kClaimBase + (K - 1 - (tid + e * T))) {
+                            const int32_t word = (fp_of(uint32_t(lx[e]), a.afp) << 16) | ls[e];
                             sQ[tgt[e]] = word;
                             gQ[tgt[e]] = word;  // written through, like C
                         } else {
@@ -728,10 +745,6 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 for (int e = 0; e < IPT; ++e)
                     c_lcol += uint32_t(__popcll(__ballot((lostm >> e) & 1u)));
             }
-
-            // Miss list (id, slot) in rank order.
-            int2* P = reinterpret_cast<int2*>(a.pairs) + tok * K;
-            for (int r = tid; r < ng; r += T) P[r] = sPair[r];
         }
 
         // Slot table and hit mask of this thread's positions.
