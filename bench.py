@@ -190,7 +190,7 @@ def probe_sweep(args):
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
     for B in (32, 128, 256, 512):
-        w = make("residency", steps=16, B=B)
+        w = make("residency", steps=40, B=B)
         cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
                                     a1=w.a1, a2=w.a2, a_fp=w.afp, flags=r.FLAG_SKIP_GATHER,
                                     stage1_threads=args.stage1_threads)
@@ -207,20 +207,22 @@ def probe_sweep(args):
         cnt0 = rs.CNT.cpu().numpy().astype(np.int64)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for t in range(8, 16):
+        timed = w.steps - 8
+        for t in range(8, w.steps):
             r.avsg_match(rs.handle, ios[t], sh)
         e1.record(stream)
         torch.cuda.synchronize()
         d = (rs.CNT.cpu().numpy().astype(np.int64) - cnt0).sum(0)
-        us = e0.elapsed_time(e1) * 1e3 / 8
-        per_step = stage1_algorithmic_bytes(B, w.S, w.Nq, d[r.CNT_LOOKUPS] / 8,
-                                            d[r.CNT_PROBE_VISITS] / 8, d[r.CNT_MISSES] / 8)
+        us = e0.elapsed_time(e1) * 1e3 / timed
+        per_step = stage1_algorithmic_bytes(B, w.S, w.Nq, d[r.CNT_LOOKUPS] / timed,
+                                            d[r.CNT_PROBE_VISITS] / timed,
+                                            d[r.CNT_MISSES] / timed)
         staged = B * (2 * 3 * w.S * 4 + w.Nq * w.K * 9)  # Q, C, F in and out + ids/outputs
         gbps = per_step / (us * 1e-6) / 1e9
         print(json.dumps({
             "probe_sweep": "residency request shape, Stage One only",
             "B": B, "K": w.K, "S": w.S, "stage1_us": round(us, 2),
-            "match_Mkeys_per_s": round(d[r.CNT_LOOKUPS] / 8 / us, 1),
+            "match_Mkeys_per_s": round(d[r.CNT_LOOKUPS] / timed / us, 1),
             "algorithmic_bytes_per_step": int(per_step),
             "achieved_GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
             "frac": round(gbps / HBM_PEAK_GBPS, 4),

@@ -23,11 +23,13 @@
 // one-barrier workgroup reductions, counters from ballots.
 //
 // Each thread owns IPT consecutive positions of a token's top-K list and
-// carries their ids through the whole token: it probes them, refreshes its
-// hits and, once it knows the rank of each of its misses among the token's
-// misses (ascending id), installs them into the victim of that rank, links
-// their bucket words and writes its slot-table and hit-mask entries with
-// vector stores.  The rank comes from a bitmap over [min id, max id] of the
+// carries their ids through the token: it probes them, refreshes its hits
+// and, once it knows the rank of each of its misses among the token's misses
+// (ascending id), installs them into the victim of that rank and writes its
+// slot-table and hit-mask entries with vector stores.  The install leaves the
+// misses in rank order in LDS, and the link runs over that list, one miss per
+// lane, so only as many waves as there are misses walk its rounds.  The rank
+// comes from a bitmap over [min id, max id] of the
 // token's misses held in LDS: one atomicOr per miss, then prefix popcounts
 // over the words, so rank(x) = (misses below x's word) + popc(word bits below
 // x).  When the ids span more than the bitmap or a missing id repeats, the
