@@ -192,31 +192,15 @@ __device__ void bitonic_sort(uint64_t* key, int P) {
     }
 }
 
-// IPT consecutive ids of one token starting at X[i0]; ids past K read as -1.
+// IPT consecutive ids of one token starting at X[i0].  The loads are
+// unconditional, from positions clamped to K - 1, and nothing selects or
+// moves their results here, so the wait for them falls at the ids' first
+// use; positions at or past K are masked to -1 there.
 template <int IPT>
-__device__ inline void load_ids(const int32_t* __restrict__ X, int i0, int K, bool vec,
+__device__ inline void load_ids(const int32_t* __restrict__ X, int i0, int K,
                                 int32_t (&x)[IPT]) {
-    if (vec && i0 + IPT <= K) {
-        if constexpr (IPT == 1) {
-            x[0] = X[i0];
-        } else if constexpr (IPT == 2) {
-            const int2 v = *reinterpret_cast<const int2*>(X + i0);
-            x[0] = v.x;
-            x[1] = v.y;
-        } else {
 #pragma unroll
-            for (int q = 0; q < IPT / 4; ++q) {
-                const int4 v = *reinterpret_cast<const int4*>(X + i0 + 4 * q);
-                x[4 * q] = v.x;
-                x[4 * q + 1] = v.y;
-                x[4 * q + 2] = v.z;
-                x[4 * q + 3] = v.w;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < IPT; ++e) x[e] = i0 + e < K ? X[i0 + e] : -1;
-    }
+    for (int e = 0; e < IPT; ++e) x[e] = X[min(i0 + e, K - 1)];
 }
 
 template <int IPT>
@@ -250,34 +234,32 @@ __device__ inline void store_outputs(int32_t* __restrict__ O, int8_t* __restrict
     }
 }
 
-// Stage nq int4 words of Q, C and F into LDS, U words per thread per pass.
+// One staging pass: int4 words j0 + u*T (u < U) of Q, C and F into LDS.
 // Branch-free so that all loads of a pass are in flight together: indices
 // past the end are clamped to the last word, and the threads that clamp
 // store that word's own value again.
 template <int T, int U, bool DENSE>
-__device__ inline void stage_words(const int32_t* gQ, const int32_t* gC, const int32_t* gF,
-                                   int32_t* sQ, int32_t* sC, uint32_t* sGw, int nq, int gadd,
-                                   int L) {
-    for (int j0 = threadIdx.x; j0 < nq; j0 += U * T) {
-        int4 q[U], c[U], f[U];
+__device__ inline void stage_pass(const int32_t* gQ, const int32_t* gC, const int32_t* gF,
+                                  int32_t* sQ, int32_t* sC, uint32_t* sGw, int j0, int nq,
+                                  int gadd, int L) {
+    int4 q[U], c[U], f[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = min(j0 + u * T, nq - 1);
-            if constexpr (!DENSE) q[u] = reinterpret_cast<const int4*>(gQ)[j];
-            c[u] = reinterpret_cast<const int4*>(gC)[j];
-            f[u] = reinterpret_cast<const int4*>(gF)[j];
-        }
+    for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u * T, nq - 1);
+        if constexpr (!DENSE) q[u] = reinterpret_cast<const int4*>(gQ)[j];
+        c[u] = reinterpret_cast<const int4*>(gC)[j];
+        f[u] = reinterpret_cast<const int4*>(gF)[j];
+    }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = min(j0 + u * T, nq - 1);
-            if constexpr (!DENSE) reinterpret_cast<int4*>(sQ)[j] = q[u];
-            reinterpret_cast<int4*>(sC)[j] = c[u];
-            const uint32_t g0 = uint32_t(min(max(f[u].x + gadd, 0), L + 1));
-            const uint32_t g1 = uint32_t(min(max(f[u].y + gadd, 0), L + 1));
-            const uint32_t g2 = uint32_t(min(max(f[u].z + gadd, 0), L + 1));
-            const uint32_t g3 = uint32_t(min(max(f[u].w + gadd, 0), L + 1));
-            sGw[j] = g0 | (g1 << 8) | (g2 << 16) | (g3 << 24);
-        }
+    for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u * T, nq - 1);
+        if constexpr (!DENSE) reinterpret_cast<int4*>(sQ)[j] = q[u];
+        reinterpret_cast<int4*>(sC)[j] = c[u];
+        const uint32_t g0 = uint32_t(min(max(f[u].x + gadd, 0), L + 1));
+        const uint32_t g1 = uint32_t(min(max(f[u].y + gadd, 0), L + 1));
+        const uint32_t g2 = uint32_t(min(max(f[u].z + gadd, 0), L + 1));
+        const uint32_t g3 = uint32_t(min(max(f[u].w + gadd, 0), L + 1));
+        sGw[j] = g0 | (g1 << 8) | (g2 << 16) | (g3 << 24);
     }
 }
 
@@ -336,20 +318,22 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     // token is fused into the load: G = max(F - 1, -1) + 1, clamped to
     // [0, L + 1] for any input.  A continuation of the step (more query
     // tokens after an earlier call) stages G = F + 1 without the decay.
+    // The first token's ids and the counters are loaded first, so that
+    // their latency overlaps the state's loads: up to two passes of staging
+    // are straight-line code, with no loop head that would wait for them.
+    int32_t xn[IPT];
+    load_ids<IPT>(a.topk + size_t(b) * a.Nq * K, i0, K, xn);
+    const int32_t cnt_old = a.CNT[size_t(b) * 8 + min(tid, 7)];  // used by tid < 8
     const int gadd = a.predecay ? 0 : 1;
     const int nq = S >> 2;  // int4 words per array
-    if (nq <= T)
-        stage_words<T, 1, DENSE>(gQ, gC, gF, sQ, sC, sGw, nq, gadd, L);
-    else if (nq <= 2 * T)
-        stage_words<T, 2, DENSE>(gQ, gC, gF, sQ, sC, sGw, nq, gadd, L);
-    else
-        stage_words<T, 4, DENSE>(gQ, gC, gF, sQ, sC, sGw, nq, gadd, L);
-    // The first token's ids and the counters are loaded after the state's
-    // loads are issued: loads pending when the staging loop starts would be
-    // waited for at its head, before any state load.
-    int32_t xn[IPT];
-    load_ids<IPT>(a.topk + size_t(b) * a.Nq * K, i0, K, vec, xn);
-    const int32_t cnt_old = tid < 8 ? a.CNT[size_t(b) * 8 + tid] : 0;
+    if (nq <= T) {
+        stage_pass<T, 1, DENSE>(gQ, gC, gF, sQ, sC, sGw, tid, nq, gadd, L);
+    } else if (nq <= 2 * T) {
+        stage_pass<T, 2, DENSE>(gQ, gC, gF, sQ, sC, sGw, tid, nq, gadd, L);
+    } else {
+        for (int j0 = tid; j0 < nq; j0 += 2 * T)
+            stage_pass<T, 2, DENSE>(gQ, gC, gF, sQ, sC, sGw, j0, nq, gadd, L);
+    }
 
     const bool row_ok = rb >= 0 && hr >= 0 && rb + hr <= a.host_rows_total;
     // The rank bitmap can cover all of the request's ids.
@@ -381,8 +365,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
 
         int32_t x[IPT];
 #pragma unroll
-        for (int e = 0; e < IPT; ++e) x[e] = xn[e];
-        if (g + 1 < a.Nq) load_ids<IPT>(a.topk + (tok + 1) * K, i0, K, vec, xn);
+        for (int e = 0; e < IPT; ++e) x[e] = i0 + e < K ? xn[e] : -1;
+        // The next token's ids (the last token reloads its own, unused).
+        load_ids<IPT>(a.topk + (g + 1 < a.Nq ? tok + 1 : tok) * K, i0, K, xn);
 
         for (int k = tid; k < kHistCopies * HB; k += T) sHist[k] = 0;
 
