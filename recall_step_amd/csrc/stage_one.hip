@@ -83,19 +83,21 @@ __device__ inline int row_scan_add(int x) { AVSG_DPP_ROW_SCAN(x, op_add, 0); ret
 __device__ inline int row_scan_min(int x) { AVSG_DPP_ROW_SCAN(x, op_min, INT32_MAX); return x; }
 __device__ inline int row_scan_max(int x) { AVSG_DPP_ROW_SCAN(x, op_max, INT32_MIN); return x; }
 
+// Workgroup reductions below take the caller's lane index (0..63).
+
 // Exclusive scan of one int per thread over the workgroup; *total gets the
 // sum.  One barrier.  scr holds kMaxWaves ints; two consecutive workgroup
 // operations must use different scratch buffers.
 template <int T>
-__device__ inline int block_excl_scan(int v, int32_t* scr, int* total) {
+__device__ inline int block_excl_scan(int v, int32_t* scr, int* total, int lane) {
     constexpr int NW = T / 64;
     const int w = threadIdx.x >> 6;
     const int incl = wave_scan_add(v);
-    if (__lane_id() == 63) scr[w] = incl;
+    if (lane == 63) scr[w] = incl;
     __syncthreads();
     // Lanes 0..NW-1 (NW <= 16: one DPP row) scan the wave totals; each wave
     // reads its prefix with one readlane.
-    const int s = row_scan_add(__lane_id() < NW ? scr[__lane_id()] : 0);
+    const int s = row_scan_add(lane < NW ? scr[lane] : 0);
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const int pre = wu > 0 ? __builtin_amdgcn_readlane(s, wu - 1) : 0;
     *total = __builtin_amdgcn_readlane(s, NW - 1);
@@ -104,33 +106,32 @@ __device__ inline int block_excl_scan(int v, int32_t* scr, int* total) {
 
 // Workgroup sum of v.  One barrier; scr holds kMaxWaves ints.
 template <int T>
-__device__ inline int block_sum(int v, int32_t* scr) {
+__device__ inline int block_sum(int v, int32_t* scr, int lane) {
     constexpr int NW = T / 64;
     const int w = threadIdx.x >> 6;
     v = lane63(wave_scan_add(v));
-    if (__lane_id() == 0) scr[w] = v;
+    if (lane == 0) scr[w] = v;
     __syncthreads();
-    return __builtin_amdgcn_readlane(row_scan_add(__lane_id() < NW ? scr[__lane_id()] : 0),
-                                     NW - 1);
+    return __builtin_amdgcn_readlane(row_scan_add(lane < NW ? scr[lane] : 0), NW - 1);
 }
 
 // Workgroup sum of v, min of lo and max of hi.  One barrier; scr holds
 // 3 * kMaxWaves ints.
 template <int T>
 __device__ inline void block_sum_min_max(int v, int lo, int hi, int32_t* scr, int* sum,
-                                         int* mn, int* mx) {
+                                         int* mn, int* mx, int lane) {
     constexpr int NW = T / 64;
     const int w = threadIdx.x >> 6;
     v = lane63(wave_scan_add(v));
     lo = lane63(wave_scan_min(lo));
     hi = lane63(wave_scan_max(hi));
-    if (__lane_id() == 0) {
+    if (lane == 0) {
         scr[w] = v;
         scr[kMaxWaves + w] = lo;
         scr[2 * kMaxWaves + w] = hi;
     }
     __syncthreads();
-    const int l = __lane_id();
+    const int l = lane;
     const bool in = l < NW;
     *sum = __builtin_amdgcn_readlane(row_scan_add(in ? scr[l] : 0), NW - 1);
     *mn = __builtin_amdgcn_readlane(row_scan_min(in ? scr[kMaxWaves + l] : INT32_MAX), NW - 1);
@@ -339,12 +340,10 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     // The rank bitmap can cover all of the request's ids.
     const bool narrow_rows = row_ok && hr > 0 && hr <= lay.bitmap_words * 32;
 
-    // This thread's contiguous run of lifetime words (4 slots each) for the
-    // S-wide passes.
+    // Each thread's contiguous run of D lifetime words (4 slots each) for the
+    // S-wide passes starts at word tid * D (taken per token below).
     const int nd = S >> 2;
     const int D = nd >= T ? nd / T : 1;  // <= 16: S <= 16384 fits LDS, T >= 256
-    const int dw0 = tid * D;
-    const int dwn = dw0 < nd ? D : 0;
 
     // Counters: c_hits, c_look and c_miss are workgroup totals (the same in
     // every thread); c_lcol, c_lexh and c_live are wave totals (from
@@ -359,17 +358,28 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     // so no load issued before it can still be pending after it.
     int g = 0;
     do {
+        // The thread's indices are taken through an opaque copy in each
+        // token, so that conditions on them (tid == 0, lane == 63, i0 + e <
+        // K, ...) are evaluated where they are used instead of being hoisted
+        // out of the loop as 64-bit lane masks, which would take the scalar
+        // registers the loop needs and spill them.
+        int tid_t = tid;
+        asm volatile("" : "+v"(tid_t));
+        const int lane_t = tid_t & 63;
+        const int i0_t = tid_t * IPT;
+        const int dw0_t = tid_t * D;
+        const int dwn_t = dw0_t < nd ? D : 0;
         const size_t tok = size_t(b) * a.Nq + g;
         int32_t* O = a.slot_table + tok * K;
         int8_t* H = a.hit_mask + tok * K;
 
         int32_t x[IPT];
 #pragma unroll
-        for (int e = 0; e < IPT; ++e) x[e] = i0 + e < K ? xn[e] : -1;
+        for (int e = 0; e < IPT; ++e) x[e] = i0_t + e < K ? xn[e] : -1;
         // The next token's ids (the last token reloads its own, unused).
-        load_ids<IPT>(a.topk + (g + 1 < a.Nq ? tok + 1 : tok) * K, i0, K, xn);
+        load_ids<IPT>(a.topk + (g + 1 < a.Nq ? tok + 1 : tok) * K, i0_t, K, xn);
 
-        for (int k = tid; k < kHistCopies * HB; k += T) sHist[k] = 0;
+        for (int k = tid_t; k < kHistCopies * HB; k += T) sHist[k] = 0;
 
         // --- Pass 1/2: probe, refresh hits, classify -----------------------
         int32_t slot[IPT];
@@ -463,12 +473,12 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         // reduced.
         int nsum, idlo, idhi;
         if (narrow_rows) {
-            nsum = block_sum<T>(m_local | (__popc(valid) << 16), sMM);
+            nsum = block_sum<T>(m_local | (__popc(valid) << 16), sMM, lane_t);
             idlo = 0;
             idhi = hr - 1;
         } else {
             block_sum_min_max<T>(m_local | (__popc(valid) << 16), lo_local, hi_local, sMM, &nsum,
-                                 &idlo, &idhi);
+                                 &idlo, &idhi, lane_t);
         }
         const int ng = min(nsum & 0xFFFF, K);
         const int nvalid = nsum >> 16;
@@ -485,9 +495,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             bool fast = span <= uint32_t(lay.bitmap_words) * 32u;
             if (fast) {
                 const int nw4 = int(((span + 31u) >> 5) + 3) & ~3;  // words, multiple of 4
-                for (int k = tid; k < (nw4 >> 2); k += T)
+                for (int k = tid_t; k < (nw4 >> 2); k += T)
                     reinterpret_cast<uint4*>(sBits)[k] = make_uint4(0, 0, 0, 0);
-                if (tid == 0) sMisc[0] = 0;
+                if (tid_t == 0) sMisc[0] = 0;
                 __syncthreads();
                 bool dup = false;
 #pragma unroll
@@ -498,21 +508,21 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                         dup |= (atomicOr(&sBits[bit >> 5], m) & m) != 0u;
                     }
                 }
-                if (__ballot(dup) != 0ull && lane == 0) sMisc[0] = 1;
+                if (__ballot(dup) != 0ull && lane_t == 0) sMisc[0] = 1;
                 __syncthreads();
                 fast = sMisc[0] == 0;
                 if (fast) {
                     // Prefix popcounts over the words, as uint16 (ng <= 8192),
                     // four words per step.
                     const int wpt = ((nw4 >> 2) + T - 1) / T * 4;
-                    const int w0 = min(tid * wpt, nw4), w1 = min(w0 + wpt, nw4);
+                    const int w0 = min(tid_t * wpt, nw4), w1 = min(w0 + wpt, nw4);
                     int cnt = 0;
                     for (int k = w0; k < w1; k += 4) {
                         const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
                         cnt += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
                     }
                     int tot;
-                    int run = block_excl_scan<T>(cnt, sS0, &tot);
+                    int run = block_excl_scan<T>(cnt, sS0, &tot, lane_t);
                     for (int k = w0; k < w1; k += 4) {
                         const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
                         const uint32_t p0 = uint32_t(run);
@@ -538,16 +548,16 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             if (!fast) {
                 // General order: bitonic sort of (id << 16 | position) keys.
                 int tot;
-                int off = block_excl_scan<T>(m_local, sS1, &tot);
+                int off = block_excl_scan<T>(m_local, sS1, &tot, lane_t);
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
                     if (missm & (1u << e))
-                        sKey[off++] = (uint64_t(uint32_t(x[e])) << 16) | uint64_t(i0 + e);
+                        sKey[off++] = (uint64_t(uint32_t(x[e])) << 16) | uint64_t(i0_t + e);
                 const int P = next_pow2(ng);
-                for (int r = ng + tid; r < P; r += T) sKey[r] = ~uint64_t(0);
+                for (int r = ng + tid_t; r < P; r += T) sKey[r] = ~uint64_t(0);
                 __syncthreads();
                 bitonic_sort<T>(sKey, P);
-                for (int r = tid; r < ng; r += T) {
+                for (int r = tid_t; r < ng; r += T) {
                     const uint64_t k = sKey[r];
                     sRank[int(k & 0xFFFFu)] = uint16_t(r);
                     if (r + 1 < ng && (k >> 16) == (sKey[r + 1] >> 16)) c_err |= 2u;
@@ -555,7 +565,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 __syncthreads();
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
-                    if (missm & (1u << e)) rank[e] = int(sRank[i0 + e]);
+                    if (missm & (1u << e)) rank[e] = int(sRank[i0_t + e]);
             }
         }
 
@@ -566,25 +576,25 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             // Each thread reads its own lifetime words from LDS in every pass
             // (loops bounded by its word count; no register copy).
             int dead_local = 0;
-            for (int q = 0; q < dwn; ++q) dead_local += __popc(zero_bytes(sGw[dw0 + q]));
+            for (int q = 0; q < dwn_t; ++q) dead_local += __popc(zero_bytes(sGw[dw0_t + q]));
             int dead_total;
-            int doff = block_excl_scan<T>(dead_local, sS0, &dead_total);
+            int doff = block_excl_scan<T>(dead_local, sS0, &dead_total, lane_t);
             if (dead_total < ng) {
-                // Histogram of G over 16 LDS copies (lane % 16 picks one).
-                int32_t* hc = sHist + (lane & (kHistCopies - 1)) * HB;
-                for (int q = 0; q < dwn; ++q) {
-                    const uint32_t gq = sGw[dw0 + q];
+                // Histogram of G over 16 LDS copies (lane_t % 16 picks one).
+                int32_t* hc = sHist + (lane_t & (kHistCopies - 1)) * HB;
+                for (int q = 0; q < dwn_t; ++q) {
+                    const uint32_t gq = sGw[dw0_t + q];
                     atomicAdd(&hc[gq & 0xFFu], 1);
                     atomicAdd(&hc[(gq >> 8) & 0xFFu], 1);
                     atomicAdd(&hc[(gq >> 16) & 0xFFu], 1);
                     atomicAdd(&hc[gq >> 24], 1);
                 }
                 __syncthreads();
-                if (tid < 64) {
+                if (tid_t < 64) {
                     // k* = least k with #{F < k} = #{G <= k} >= ng.
                     int carry = 0, kstar = -1;
                     for (int base = 0; base < HB && kstar < 0; base += 64) {
-                        const int k = base + lane;
+                        const int k = base + lane_t;
                         int hv = 0;
                         if (k < HB)
                             for (int c = 0; c < kHistCopies; ++c) hv += sHist[c * HB + k];
@@ -593,30 +603,30 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                         if (reach) kstar = base + __ffsll((unsigned long long)reach) - 1;
                         carry = lane63(cum);
                     }
-                    if (lane == 0) sMisc[1] = kstar < 0 ? L + 1 : kstar;
+                    if (lane_t == 0) sMisc[1] = kstar < 0 ? L + 1 : kstar;
                 }
                 __syncthreads();
                 const uint32_t kstar = uint32_t(sMisc[1]);
                 dead_local = 0;
-                for (int q = 0; q < dwn; ++q) {
-                    const uint32_t gq = sGw[dw0 + q];
+                for (int q = 0; q < dwn_t; ++q) {
+                    const uint32_t gq = sGw[dw0_t + q];
                     uint32_t r = 0;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t v = (gq >> (8 * j)) & 0xFFu;
                         r |= (v > kstar ? v - kstar : 0u) << (8 * j);
                     }
-                    sGw[dw0 + q] = r;
+                    sGw[dw0_t + q] = r;
                     dead_local += __popc(zero_bytes(r));
                 }
-                doff = block_excl_scan<T>(dead_local, sS1, &dead_total);
+                doff = block_excl_scan<T>(dead_local, sS1, &dead_total, lane_t);
             }
             // CollectDead: the ng lowest-index dead slots, in slot order.
-            for (int q = 0; q < dwn && doff < ng; ++q) {
-                uint32_t z = zero_bytes(sGw[dw0 + q]);
+            for (int q = 0; q < dwn_t && doff < ng; ++q) {
+                uint32_t z = zero_bytes(sGw[dw0_t + q]);
                 while (z && doff < ng) {
                     const int j = (__ffs(int(z)) - 1) >> 3;
-                    sVict[doff++] = (dw0 + q) * 4 + j;
+                    sVict[doff++] = (dw0_t + q) * 4 + j;
                     z &= z - 1u;
                 }
             }
@@ -654,21 +664,21 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                                                __HIP_MEMORY_SCOPE_AGENT);
                 // Miss list (id, slot) in rank order.
                 int2* P = reinterpret_cast<int2*>(a.pairs) + tok * K;
-                for (int r = tid; r < ng; r += T) P[r] = sPair[r];
+                for (int r = tid_t; r < ng; r += T) P[r] = sPair[r];
             } else {
                 // --- Link: first reusable bucket in R+1 rounds, judged on the
                 // bucket words before this token's writes and the slots after its
                 // installs; one scatter, the largest rank keeps a contested bucket.
-                // Thread tid links the misses of rank tid + e*T, read from the
+                // Thread tid_t links the misses of rank tid_t + e*T, read from the
                 // rank-ordered pairs: the ng misses fill the first waves one per
-                // lane and the other waves leave at the first round, where a
+                // lane_t and the other waves leave at the first round, where a
                 // link by the owning thread keeps every wave walking the rounds.
                 int32_t lx[IPT], ls[IPT], tgt[IPT];
                 uint32_t lp[IPT], ld[IPT];
                 uint32_t search = 0;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
-                    const int r = tid + e * T;
+                    const int r = tid_t + e * T;
                     const int2 pr = r < ng ? sPair[r] : make_int2(0, 0);
                     lx[e] = pr.x;
                     ls[e] = pr.y;
@@ -681,7 +691,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 int2* P = reinterpret_cast<int2*>(a.pairs) + tok * K;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
-                    if ((search >> e) & 1u) P[tid + e * T] = make_int2(lx[e], ls[e]);
+                    if ((search >> e) & 1u) P[tid_t + e * T] = make_int2(lx[e], ls[e]);
                 // Checked every round: most links succeed in the first.
                 for (int t = 0; t <= R; ++t) {
                     if (__ballot(search != 0u) == 0ull) break;
@@ -713,13 +723,13 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 __syncthreads();
 #pragma unroll
                 for (int e = 0; e < IPT; ++e)
-                    if (tgt[e] >= 0) atomicMin(&sQ[tgt[e]], kClaimBase + (K - 1 - (tid + e * T)));
+                    if (tgt[e] >= 0) atomicMin(&sQ[tgt[e]], kClaimBase + (K - 1 - (tid_t + e * T)));
                 __syncthreads();
                 uint32_t lostm = 0;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
                     if (tgt[e] >= 0) {
-                        if (sQ[tgt[e]] == kClaimBase + (K - 1 - (tid + e * T))) {
+                        if (sQ[tgt[e]] == kClaimBase + (K - 1 - (tid_t + e * T))) {
                             const int32_t word = (fp_of(uint32_t(lx[e]), a.afp) << 16) | ls[e];
                             sQ[tgt[e]] = word;
                             gQ[tgt[e]] = word;  // written through, like C
@@ -743,8 +753,8 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             o[e] = ok ? slot[e] : -1;
             hm[e] = ok ? int8_t(((missm >> e) & 1u) ? 0 : 1) : int8_t(-1);
         }
-        store_outputs<IPT>(O, H, i0, K, vec, o, hm);
-        if (tid == 0) a.n_miss[tok] = ng;
+        store_outputs<IPT>(O, H, i0_t, K, vec, o, hm);
+        if (tid_t == 0) a.n_miss[tok] = ng;
         __syncthreads();
     } while (++g < a.Nq);
 
