@@ -172,6 +172,12 @@ __device__ inline uint32_t zero_bytes(uint32_t x) {
     return ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
 }
 
+// Zero n LDS words (n a multiple of 4), one 16-byte store per thread and pass.
+template <int T>
+__device__ inline void clear_words(uint32_t* w, int n, int tid) {
+    for (int k = tid; k < (n >> 2); k += T) reinterpret_cast<uint4*>(w)[k] = make_uint4(0, 0, 0, 0);
+}
+
 // Ascending bitonic sort of P (a power of two) 64-bit keys in LDS.
 template <int T>
 __device__ void bitonic_sort(uint64_t* key, int P) {
@@ -352,10 +358,16 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     uint32_t c_lcol = 0, c_lexh = 0, c_live = 0;
     uint32_t c_visit = 0, c_err = 0;
 
+    // The rank bitmap starts every token clear: it is cleared here, while
+    // the staging loads are in flight, and again after each token that used
+    // it, so the rank pass needs no clear and barrier of its own.
+    clear_words<T>(sBits, lay.bitmap_words, tid);
+    if (tid == 0) sMisc[0] = 0;  // repeated-id flag
     __syncthreads();
 
     // N_q >= 1: a do-while leaves no path on which the loop body is skipped,
     // so no load issued before it can still be pending after it.
+    bool region_dirty = false;  // dense matcher: the last token used the bitmap region
     int g = 0;
     do {
         // The thread's indices are taken through an opaque copy in each
@@ -372,6 +384,11 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         const size_t tok = size_t(b) * a.Nq + g;
         int32_t* O = a.slot_table + tok * K;
         int8_t* H = a.hit_mask + tok * K;
+
+        // The dense matcher reads the pairs until the previous token's last
+        // barrier, so it clears the bitmap here instead.
+        if constexpr (DENSE)
+            if (region_dirty) clear_words<T>(sBits, lay.bitmap_words, tid_t);
 
         int32_t x[IPT];
 #pragma unroll
@@ -490,15 +507,14 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         int32_t rank[IPT];
 #pragma unroll
         for (int e = 0; e < IPT; ++e) rank[e] = -1;
+        // Dead-slot prefix and total, when the rank scan counted them (-1:
+        // not counted).
+        int dead_pre = -1, dead_all = -1;
         if (ng > 0) {
             const uint32_t span = uint32_t(idhi) - uint32_t(idlo) + 1u;  // ids >= 0
             bool fast = span <= uint32_t(lay.bitmap_words) * 32u;
             if (fast) {
                 const int nw4 = int(((span + 31u) >> 5) + 3) & ~3;  // words, multiple of 4
-                for (int k = tid_t; k < (nw4 >> 2); k += T)
-                    reinterpret_cast<uint4*>(sBits)[k] = make_uint4(0, 0, 0, 0);
-                if (tid_t == 0) sMisc[0] = 0;
-                __syncthreads();
                 bool dup = false;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
@@ -513,7 +529,11 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 fast = sMisc[0] == 0;
                 if (fast) {
                     // Prefix popcounts over the words, as uint16 (ng <= 8192),
-                    // four words per step.
+                    // four words per step.  The same scan also takes the
+                    // dead-slot counts of the victim pass (refreshes are
+                    // done, installs not begun), packed above the bit counts:
+                    // both totals stay below 2^16 (ng <= K <= 8192, S <=
+                    // 16384), so the low half never carries.
                     const int wpt = ((nw4 >> 2) + T - 1) / T * 4;
                     const int w0 = min(tid_t * wpt, nw4), w1 = min(w0 + wpt, nw4);
                     int cnt = 0;
@@ -521,8 +541,14 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                         const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
                         cnt += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
                     }
+                    int dead_local = 0;
+                    for (int q = 0; q < dwn_t; ++q)
+                        dead_local += __popc(zero_bytes(sGw[dw0_t + q]));
                     int tot;
-                    int run = block_excl_scan<T>(cnt, sS0, &tot, lane_t);
+                    int run = block_excl_scan<T>(cnt | (dead_local << 16), sS0, &tot, lane_t);
+                    dead_pre = run >> 16;
+                    dead_all = tot >> 16;
+                    run &= 0xFFFF;
                     for (int k = w0; k < w1; k += 4) {
                         const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
                         const uint32_t p0 = uint32_t(run);
@@ -576,9 +602,12 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             // Each thread reads its own lifetime words from LDS in every pass
             // (loops bounded by its word count; no register copy).
             int dead_local = 0;
-            for (int q = 0; q < dwn_t; ++q) dead_local += __popc(zero_bytes(sGw[dw0_t + q]));
-            int dead_total;
-            int doff = block_excl_scan<T>(dead_local, sS0, &dead_total, lane_t);
+            int dead_total = dead_all;
+            int doff = dead_pre;
+            if (dead_all < 0) {
+                for (int q = 0; q < dwn_t; ++q) dead_local += __popc(zero_bytes(sGw[dw0_t + q]));
+                doff = block_excl_scan<T>(dead_local, sS0, &dead_total, lane_t);
+            }
             if (dead_total < ng) {
                 // Histogram of G over 16 LDS copies (lane_t % 16 picks one).
                 int32_t* hc = sHist + (lane_t & (kHistCopies - 1)) * HB;
@@ -725,6 +754,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                 for (int e = 0; e < IPT; ++e)
                     if (tgt[e] >= 0) atomicMin(&sQ[tgt[e]], kClaimBase + (K - 1 - (tid_t + e * T)));
                 __syncthreads();
+                // Every read of the pairs and of the bitmap is done: clear it
+                // for the next token.
+                if (g + 1 < a.Nq) clear_words<T>(sBits, lay.bitmap_words, tid_t);
                 uint32_t lostm = 0;
 #pragma unroll
                 for (int e = 0; e < IPT; ++e) {
@@ -755,6 +787,8 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         }
         store_outputs<IPT>(O, H, i0_t, K, vec, o, hm);
         if (tid_t == 0) a.n_miss[tok] = ng;
+        if (ng > 0 && tid_t == 0) sMisc[0] = 0;  // read before two barriers at least
+        if constexpr (DENSE) region_dirty = ng > 0;
         __syncthreads();
     } while (++g < a.Nq);
 
