@@ -127,6 +127,43 @@ def test_wide_id_span_takes_the_sorting_path():
     assert cnt[0] > 0 and cnt[5] > 0
 
 
+def test_query_tokens_switch_between_sorting_and_the_rank_bitmap():
+    """Three query tokens per step, each ordering its misses either with the
+    rank bitmap (ids below 2^16) or by sorting (ids up to 2^30, or a missing
+    id repeated), in a pattern that changes with step and request.  So a
+    token often starts after one that left the shared LDS region full of
+    sort keys, miss pairs or bitmap bits.  Each token also selects a quarter
+    of the previous token's ids, which that token installed: hits within the
+    step."""
+    K, S, Nq, B, steps, hr = 512, 2048, 3, 3, 6, 1 << 30
+    rng = np.random.default_rng([23, K, S, Nq])
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    for t in range(steps):
+        for b in range(B):
+            prev = None
+            for g in range(Nq):
+                mode = (t + b + g) % 3
+                n_keep = 0 if prev is None else K // 4
+                keep = (rng.choice(prev, n_keep, replace=False) if n_keep
+                        else np.zeros(0, np.int64))
+                hi = (1 << 30) if mode == 0 else (1 << 16)
+                fresh = np.setdiff1d(rng.choice(hi, K + n_keep, replace=False), keep)
+                fresh = rng.permutation(fresh)[: K - n_keep]
+                if mode == 2:
+                    fresh[-1] = fresh[0]  # one missing id twice
+                ids = rng.permutation(np.concatenate([keep, fresh])).astype(np.int32)
+                topk[t, b, g] = ids
+                prev = np.unique(ids)
+    w = make("matching", steps=steps)
+    w.name, w.topk, w.B, w.Nq, w.K, w.S, w.steps = ("tokens switch order paths", topk, B, Nq,
+                                                    K, S, steps)
+    w.ctx_len = np.full((steps, B), hr, np.int32)
+    w.host_rows = np.full(B, hr, np.int32)
+    w.row_base = np.arange(B, dtype=np.int64) * hr
+    cnt = run_parity(w, gather=False)
+    assert (cnt[:, 6] & 2).all() and cnt[:, 0].sum() > 0
+
+
 def test_repeated_missing_ids_take_the_sorting_path():
     """A token that misses the same id twice: both copies get slots in
     (id, position) order and the duplicate error bit is set."""
