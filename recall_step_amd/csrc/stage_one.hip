@@ -306,10 +306,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     int32_t* gQ = a.Q + size_t(b) * S;
     int32_t* gC = a.C + size_t(b) * S;
     int32_t* gF = a.F + size_t(b) * S;
-    // Vector loads and stores of a thread's IPT positions need K % IPT == 0
-    // and base pointers aligned to the vector size.
+    // Vector stores of a thread's IPT output positions need K % IPT == 0 and
+    // base pointers aligned to the vector size.
     const bool vec = (K % IPT) == 0 &&
-                     (reinterpret_cast<uintptr_t>(a.topk) % (4 * IPT)) == 0 &&
                      (reinterpret_cast<uintptr_t>(a.slot_table) % (4 * IPT)) == 0 &&
                      (reinterpret_cast<uintptr_t>(a.hit_mask) % IPT) == 0;
     const int i0 = tid * IPT;
@@ -659,6 +658,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                     z &= z - 1u;
                 }
             }
+            // Besides publishing the victims, this barrier keeps the install's
+            // pairs (sPair aliases the rank bitmap and its prefix counts) from
+            // overwriting words that a slower thread still reads for a rank.
             __syncthreads();
 
             // --- Install the r-th smallest miss into the r-th victim ---------
