@@ -127,6 +127,22 @@ def test_wide_id_span_takes_the_sorting_path():
     assert cnt[0] > 0 and cnt[5] > 0
 
 
+@pytest.mark.parametrize("K,S,threads,gather", [(333, 1024, 0, False), (1001, 2048, 0, True),
+                                                (1001, 2048, 256, False),
+                                                (2001, 4096, 256, False)])
+def test_token_length_not_a_multiple_of_ids_per_thread(K, S, threads, gather):
+    """K that the ids per thread (2, 4 or 8 here) do not divide: one thread
+    owns positions on both sides of K, whose ids past K must read as padding,
+    and the outputs go out with scalar stores.  Ids come from a universe of
+    3K, so about a third repeat from step to step."""
+    def draw(rng, t, b):
+        return rng.choice(3 * K, K, replace=False).astype(np.int32)
+
+    w = _stage_one_only(f"K={K} threads={threads}", K, S, 5, 3, 3 * K, draw)
+    cnt = run_parity(w, gather=gather, stage1_threads=threads)
+    assert cnt[:, 0].sum() > 0 and cnt[:, 1].sum() == 5 * 3 * K
+
+
 def test_query_tokens_switch_between_sorting_and_the_rank_bitmap():
     """Three query tokens per step, each ordering its misses either with the
     rank bitmap (ids below 2^16) or by sorting (ids up to 2^30, or a missing
