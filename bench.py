@@ -721,6 +721,22 @@ def cpu_baseline(w, host_array, warmup, steps, budget_s):
     return statistics.median(per_pass), passes
 
 
+def adjacent_step_reuse(topk, t0, t1):
+    """Mean over requests and steps t in [t0, t1) of the fraction of step t's
+    selected ids (all query tokens, padding and repeats dropped) that step
+    t - 1 selected too; None when t0 is 0."""
+    if t0 < 1:
+        return None
+    fr = []
+    for t in range(t0, t1):
+        for b in range(topk.shape[1]):
+            cur = np.unique(topk[t, b][topk[t, b] >= 0])
+            prev = np.unique(topk[t - 1, b][topk[t - 1, b] >= 0])
+            if cur.size:
+                fr.append(np.isin(cur, prev, assume_unique=True).mean())
+    return float(np.mean(fr)) if fr else None
+
+
 def host_threads():
     """Worker threads for host-side work: the machine's CPU share (its
     OMP_NUM_THREADS), else the visible cores."""
@@ -807,8 +823,15 @@ def main():
     sh = stream.cuda_stream
     torch.cuda.synchronize()
 
+    first_reuse = None
     for t in range(args.warmup):
         rs.step(ios[t % w.steps], stream)
+        if t == 0:
+            # The first step starts from an empty buffer: whatever it does
+            # not copy, its query tokens reused from one another.
+            d0 = rs.CNT.cpu().numpy().astype(np.int64).sum(0)
+            if d0[r.CNT_LOOKUPS]:
+                first_reuse = 1.0 - d0[r.CNT_MISSES] / d0[r.CNT_LOOKUPS]
     torch.cuda.synchronize()
     cnt0 = rs.CNT.cpu().numpy().astype(np.int64)
 
@@ -873,6 +896,8 @@ def main():
 
     s1_bytes_step = stage1_algorithmic_bytes(w.B, w.S, w.Nq, lookups / K, visits / K,
                                              misses / K)
+    adj_reuse = (adjacent_step_reuse(w.topk, args.warmup, args.warmup + K)
+                 if w.steps >= args.warmup + K else None)
 
     result = {
         "metric": METRIC,
@@ -902,6 +927,8 @@ def main():
         "misses_per_step": round(misses / K, 1),
         "hit_rate": round(hits / lookups, 4) if lookups else 0.0,
         "lost_mappings_per_step": round(float(d[r.CNT_LOST_COLLISION] + d[r.CNT_LOST_EXHAUSTED]) / K, 1),
+        "adjacent_reuse": (None if adj_reuse is None else round(adj_reuse, 4)),
+        "first_step_reuse": (None if first_reuse is None else round(float(first_reuse), 4)),
         "roofline": {
             "bound": "pcie",
             "achieved": round(gather_gbps, 2),

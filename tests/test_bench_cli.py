@@ -1,13 +1,15 @@
 """The bench's host-side contract (no GPU needed): it refuses more than one
 GPU with a message, reports the profiled gather traffic only for the gather
-sources the profile was taken on, and prices Stage One's algorithmic bytes
-by the unit costs it documents."""
+sources the profile was taken on, prices Stage One's algorithmic bytes by
+the unit costs it documents, and measures adjacent-step reuse by the
+page's definition."""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -50,3 +52,16 @@ def test_step_counts_are_validated():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "--steps" in r.stderr
+
+
+def test_adjacent_step_reuse_follows_the_rate_definition():
+    """The bench's adjacent-step reuse is the mean, over requests and steps,
+    of the page's definition as the oracle's rate module states it."""
+    from oracle import rates
+    from workloads import make
+    for name in ("tiny", "matching"):
+        w = make(name, steps=6)
+        expect = np.mean([rates.adjacent_reuse(w.topk[t - 1, b], w.topk[t, b])
+                          for t in range(2, 6) for b in range(w.B)])
+        assert bench.adjacent_step_reuse(w.topk, 2, 6) == pytest.approx(expect, abs=1e-12)
+    assert bench.adjacent_step_reuse(w.topk, 0, 6) is None
