@@ -896,8 +896,9 @@ def main():
 
     s1_bytes_step = stage1_algorithmic_bytes(w.B, w.S, w.Nq, lookups / K, visits / K,
                                              misses / K)
-    adj_reuse = (adjacent_step_reuse(w.topk, args.warmup, args.warmup + K)
-                 if w.steps >= args.warmup + K else None)
+    # Over the distinct timed steps (a workload with fewer steps than the run
+    # replays them cyclically).
+    adj_reuse = adjacent_step_reuse(w.topk, args.warmup, min(args.warmup + K, w.steps))
 
     result = {
         "metric": METRIC,
