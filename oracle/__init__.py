@@ -33,26 +33,44 @@ RC_NAMES = {0: "ok", -1: "bad argument", -2: "slot referenced earlier in the "
             "step was evicted", -3: "lifetime out of range", -4: "out of memory"}
 
 
-def build() -> str:
-    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
-    tmp = _LIB + ".tmp"
+# Extra gcc flags of a sanitizer build (see build(sanitize=True)).
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+
+
+def build(src: str = _SRC, out: str = _LIB, sanitize: bool = False) -> str:
+    """Compile the oracle source ``src`` with gcc into the shared library
+    ``out`` (by default ``oracle/liboracle.so``).  ``sanitize`` builds it
+    with AddressSanitizer and UndefinedBehaviorSanitizer; such a library is
+    loaded by a process started with the sanitizer runtimes preloaded."""
+    tmp = out + ".tmp"
     # -ffp-contract=off: float32 products and sums round one at a time.
-    subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror",
-                    "-ffp-contract=off", "-shared", "-fPIC", "-o", tmp, _SRC,
-                    "-lm"], check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    flags = ["-std=c11", "-Wall", "-Wextra", "-Werror", "-ffp-contract=off",
+             "-shared", "-fPIC"]
+    flags = (SANITIZE_FLAGS if sanitize else ["-O2"]) + flags
+    subprocess.run(["gcc", *flags, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
 
 
+def library_path() -> str:
+    """The library the wrapper loads: ``$AVSG_ORACLE_LIB`` when set (a
+    sanitizer or test build made by build(); used as is, never rebuilt),
+    else ``oracle/liboracle.so``, rebuilt when older than its source."""
+    return os.environ.get("AVSG_ORACLE_LIB") or _LIB
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        path = library_path()
+        if path == _LIB and (not os.path.exists(_LIB) or
+                             os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         lib.orc_step.argtypes = [p] * 15
         lib.orc_step.restype = ctypes.c_int

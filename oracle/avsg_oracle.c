@@ -163,8 +163,10 @@ int orc_step(const orc_cfg* cfg, int32_t* Qall, int32_t* Call, int32_t* Fall,
              int32_t* miss_pairs)
 {
     const int32_t B = cfg->B, Nq = cfg->Nq, K = cfg->K, S = cfg->S, L = cfg->L;
+    /* R <= S - 1: an odd stride modulo a power of two has visited every
+     * bucket after S rounds, so further rounds would only revisit them. */
     if (B < 0 || Nq < 1 || K < 1 || S < 1 || (S & (S - 1)) != 0 || S > 65536 ||
-        (int64_t)Nq * K > S || L < 1 || L > 127 || cfg->R < 0)
+        (int64_t)Nq * K > S || L < 1 || L > 127 || cfg->R < 0 || cfg->R > S - 1)
         return ORC_EARG;
 
     orc_miss* misses = (orc_miss*)malloc(sizeof(orc_miss) * (size_t)K);

@@ -198,6 +198,55 @@ def test_duplicate_ids_flagged_and_kept_separate():
     assert s[0] != s[1] and min(s[:3]) >= 0
 
 
+def _run_matcher(o, kind, topk, ctx, row_base, host_rows, map_len=100):
+    if kind == "hash":
+        return o.step(topk, ctx, row_base, host_rows)
+    if kind == "dense":
+        return o.step_dense(topk, ctx, row_base, host_rows, map_len)
+    if kind == "sort_merge":
+        return o.step_sort_merge(topk, ctx, row_base, host_rows)
+    return o.step_no_reuse(topk, ctx, row_base, host_rows)
+
+
+@pytest.mark.parametrize("kind", ["hash", "dense", "sort_merge", "no_reuse"])
+def test_edge_inputs_of_every_matcher(kind):
+    """Edge inputs through each step function: a verified length N <= 0
+    empties every slot at the end of the step (every id is >= 0 >= N; App. B,
+    Speculative Invalidation), so the next step misses everything; a token of
+    padding only looks nothing up; a request with no host rows treats every
+    id as out of range.  Request 0 is normal, 1 has N = 0, 2 has N = -5, 3
+    selects only padding, 4 has no host rows."""
+    B, Nq, K, S = 5, 2, 4, 16
+    o = Oracle(B, Nq, K, S, 2, 3, 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D, 16, 500)
+    # distinct residues mod S: distinct home buckets (a1 is odd), nothing lost
+    X = np.tile(np.array([3, 8, 50, 69], np.int32), (B, Nq, 1))
+    X[3] = -1
+    ctx = np.array([100, 0, -5, 100, 100], np.int32)
+    row_base = np.arange(B, dtype=np.int64) * 100
+    host_rows = np.array([100, 100, 100, 100, 0], np.int32)
+    for step in range(3):
+        out = _run_matcher(o, kind, X, ctx, row_base, host_rows)
+        assert (out.hit_mask[3] == -1).all() and (out.slot_table[3] == -1).all()
+        assert (out.hit_mask[4] == -1).all() and (out.n_miss[3:] == 0).all()
+        assert o.CNT[3, oracle.LOOKUPS] == 0 and o.CNT[4, oracle.LOOKUPS] == 0
+        assert o.CNT[4, oracle.ERRORS] == oracle.ERR_OUT_OF_RANGE
+        assert o.CNT[3, oracle.ERRORS] == 0
+        for b in (0, 1, 2):
+            assert o.CNT[b, oracle.LOOKUPS] == (step + 1) * Nq * K
+        if kind == "no_reuse":
+            continue
+        for b in (1, 2):
+            assert (o.C[b] == -1).all()
+            # only the first token of each step copies: the later one hits
+            # the rows the first one filled within the step
+            assert out.n_miss[b].tolist() == [K, 0]
+        if kind == "dense":
+            assert (o.map[1:3] == -1).all()
+        if step > 0:
+            assert (out.hit_mask[0] == 1).all()
+    assert (o.C[3] == -1).all() and (o.C[4] == -1).all()
+
+
 def test_lifetime_survives_L_decays_then_dies():
     """A slot set to L stays reusable-protected for L unit decays and is
     reclaimable after L+1 (section 3.5; App. B slot preservation)."""
@@ -332,6 +381,17 @@ def test_invariants_on_workloads(name):
         assert o.F.min() >= -1 and o.F.max() <= w.L
         c = o.CNT.astype(np.int64)
         assert (c[:, oracle.HITS] + c[:, oracle.MISSES] == c[:, oracle.LOOKUPS]).all()
+
+
+def test_probe_rounds_beyond_the_buckets_are_refused():
+    """R + 1 > S rounds would only revisit buckets (odd stride modulo a
+    power of two, section 3.3), so the oracle refuses R > S - 1 and accepts
+    R = S - 1."""
+    X = np.array([[[1, 2]]], np.int32)
+    args = (np.array([100], np.int32), np.zeros(1, np.int64), np.array([100], np.int32))
+    Oracle(1, 1, 2, 16, 2, 15, 1, 1, 1, 16, 100).step(X, *args)
+    with pytest.raises(oracle.OracleError):
+        Oracle(1, 1, 2, 16, 2, 16, 1, 1, 1, 16, 100).step(X, *args)
 
 
 def test_capacity_bound_is_enforced():
@@ -474,6 +534,88 @@ def test_sort_merge_hits_are_the_set_intersection(seed):
             assert np.array_equal(o.shadow[b, v], hk[lo:lo + w.row_bytes])
 
 
+def _sort_merge_oracle(case):
+    p = case["params"]
+    return Oracle(p["B"], p["Nq"], p["K"], p["S"], p["L"], p["R"], p["a1"], p["a2"],
+                  p["afp"], p["row_bytes"], case["host_rows"])
+
+
+def test_sort_merge_handworked_two_tokens():
+    """Three steps of two query tokens worked by hand (derivations in the
+    fixture): a later token's misses skip every row an earlier token of the
+    same step hit or filled, an id cached in two rows hits the lower one, a
+    row filled earlier in the step is a hit for a later token, and the rows
+    of ids at or beyond N are emptied at the end of the step (AVSG page,
+    sections 2, 3.6 and 4.2)."""
+    with open(os.path.join(GOLDEN, "sort_merge_nq2_s8.json")) as f:
+        case = json.load(f)
+    o = _sort_merge_oracle(case)
+    hr = case["host_rows"]
+    for st in case["steps"]:
+        out = o.step_sort_merge(np.asarray(st["topk"], np.int32).reshape(1, o.Nq, o.K),
+                                np.array([st["ctx_len"]], np.int32),
+                                np.zeros(1, np.int64), np.array([hr], np.int32))
+        assert out.slot_table[0].tolist() == st["slot_table"]
+        assert out.hit_mask[0].tolist() == st["hit_mask"]
+        assert out.n_miss[0].tolist() == st["n_miss"]
+        for g, n in enumerate(st["n_miss"]):
+            assert out.miss_pairs[0, g, :n].tolist() == st["miss_pairs"][g]
+        assert o.C[0].tolist() == st["C"]
+        assert o.CNT[0].tolist() == st["CNT"]
+
+
+@pytest.mark.parametrize("Nq", [2, 3, 4])
+def test_sort_merge_identical_tokens_from_empty_reuse_closed_form(Nq):
+    """N_q query tokens selecting the same K distinct ids from an empty
+    buffer: the first token copies all K, every later token hits all K in
+    the rows the first one filled, so reuse = (N_q - 1) / N_q exactly (the
+    page's first-iteration reuse, section 4.4, for identical tokens)."""
+    K, S = 32, 128
+    rng = np.random.default_rng(Nq)
+    X = rng.choice(5000, K, replace=False).astype(np.int32)
+    o = Oracle(1, Nq, K, S, 3, 7, 1, 3, 5, 16, 5000)
+    out = o.step_sort_merge(np.tile(X, (1, Nq, 1)), np.array([5000], np.int32),
+                            np.zeros(1, np.int64), np.array([5000], np.int32))
+    assert (out.hit_mask[0, 0] == 0).all()
+    assert (out.hit_mask[0, 1:] == 1).all()
+    for g in range(1, Nq):
+        assert out.slot_table[0, g].tolist() == out.slot_table[0, 0].tolist()
+    hits, lookups = int(o.CNT[0, oracle.HITS]), int(o.CNT[0, oracle.LOOKUPS])
+    assert hits * Nq == (Nq - 1) * lookups
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sort_merge_first_step_hits_are_overlaps_with_earlier_tokens(seed):
+    """From an empty buffer, with N_q*K <= S, token g hits exactly the ids it
+    shares with tokens 0..g-1 of the same step: every id an earlier token
+    selected holds a row that no later token of the step may take (the page's
+    progressive reuse across the tokens of one step, sections 3.6 and 4.4).
+    Set arithmetic on the inputs, no buffer model."""
+    rng = np.random.default_rng([seed, 11])
+    Nq, K = int(rng.integers(2, 5)), int(rng.integers(4, 24))
+    S = 1 << int(np.ceil(np.log2(Nq * K)))
+    base = rng.choice(200, K, replace=False)
+    X = np.empty((Nq, K), np.int32)
+    for g in range(Nq):
+        keep = rng.random(K) < 0.5
+        fresh = rng.choice(np.setdiff1d(np.arange(400), base), K, replace=False)
+        # distinct within the token; fresh draws of two tokens may coincide
+        X[g] = np.where(keep, base, fresh)
+        rng.shuffle(X[g])
+    o = Oracle(1, Nq, K, S, 3, 7, 1, 3, 5, 16, 400)
+    out = o.step_sort_merge(X.reshape(1, Nq, K), np.array([400], np.int32),
+                            np.zeros(1, np.int64), np.array([400], np.int32))
+    seen = set()
+    for g in range(Nq):
+        expect = np.isin(X[g], list(seen)) if seen else np.zeros(K, bool)
+        assert np.array_equal(out.hit_mask[0, g] == 1, expect), g
+        assert int(out.n_miss[0, g]) == int((~expect).sum())
+        seen |= set(X[g].tolist())
+    # every selected id of the step ends up cached, each in its own row
+    cached = o.C[0][o.C[0] >= 0]
+    assert sorted(cached.tolist()) == sorted(seen)
+
+
 def test_sort_merge_with_s_equal_k_tracks_adjacent_step_reuse():
     """S = K and full, distinct selections: the buffer ends every step holding
     exactly that step's ids, so the hit rate of step t is the adjacent-step
@@ -543,10 +685,12 @@ def test_ema_threshold_closes_the_gap_by_one_minus_alpha():
     s = np.array([2.0, -1.5], np.float32)
     th = Oracle.ema_threshold(s, np.full(2, np.inf, np.float32), 0.5)
     assert np.array_equal(th, s)
-    th = np.array([10.0, 6.5], np.float32)
-    for n in range(1, 12):
-        th = Oracle.ema_threshold(s, th, 0.5)
-        assert np.allclose(th - s, (np.array([8.0, 8.0]) * 0.5 ** n), rtol=0, atol=1e-6)
+    for alpha in (0.5, 0.25, 0.75, 1.0):
+        th = np.array([10.0, 6.5], np.float32)
+        for n in range(1, 12):
+            th = Oracle.ema_threshold(s, th, alpha)
+            assert np.allclose(th - s, (np.array([8.0, 8.0]) * (1 - alpha) ** n),
+                               rtol=0, atol=1e-5), (alpha, n)
 
 
 # --- dense id -> slot map (ECHO page, GPU cache manager) -------------------
