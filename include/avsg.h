@@ -129,7 +129,9 @@ typedef struct avsg_config {
     int32_t L;         /* lifetime given on refresh or install, 1..127
                           (AVSG s3.5) */
     int32_t R;         /* probe rounds beyond the first: a lookup examines up
-                          to R+1 buckets (AVSG s3.3 "Probe primitive"), >= 0 */
+                          to R+1 buckets (AVSG s3.3 "Probe primitive"),
+                          0..S-1 (the odd stride has visited every bucket
+                          after S rounds; larger R is AVSG_EINVAL) */
     uint32_t a1;       /* odd multiplier of the home bucket (a1*x) mod S */
     uint32_t a2;       /* odd multiplier of the stride ((a2*x) mod S) | 1 */
     uint32_t a_fp;     /* odd multiplier of the 15-bit fingerprint
@@ -222,19 +224,27 @@ size_t avsg_stage1_lds_bytes(const avsg_config* cfg);
 size_t avsg_workspace_bytes(const avsg_config* cfg);
 
 /* Validate cfg and bufs, resolve the device alias of host_kv, allocate the
- * workspace and return a handle in *out.  Enqueues no work; the state
- * buffers must be initialised with avsg_state_init before the first step.
- * On failure *out is NULL and nothing is leaked. */
+ * workspace and return a handle in *out.  The handle binds, per request, the
+ * device buffer of S slots carried across decode steps (AVSG s3.1, Figure
+ * 2) and its metadata table of bucket words, cached ids and lifetimes (AVSG
+ * s3.2, the Hash-State table).  Enqueues
+ * no work; the state buffers must be initialised with avsg_state_init
+ * before the first step.  On failure *out is NULL and nothing is leaked. */
 int avsg_create(const avsg_config* cfg, const avsg_buffers* bufs,
                 avsg_handle** out);
 
-/* Free the handle and its workspace (not the caller's buffers).  NULL is
+/* Release what avsg_create allocated: the handle and its workspace (not the
+ * caller's buffers, which hold the slot buffer of AVSG s3.1).  NULL is
  * accepted.  Work already enqueued must have finished. */
 int avsg_destroy(avsg_handle* h);
 
-/* Enqueue a reset of request rows to the empty state: Q = C = F = -1,
- * CNT = 0 (and, with AVSG_FLAG_DENSE_MAP, every map entry -1).  row_mask: device int32 [B], nonzero = reset that row; NULL =
- * all rows.  Uses a kernel (no hipMemset). */
+/* Enqueue a reset of request rows to the empty state: no bucket word, no
+ * cached id and every slot dead (AVSG s3.5: a dead slot is reclaimable; App.
+ * B: bucket words pack a fingerprint and a slot), i.e. Q = C = F = -1,
+ * CNT = 0 (and, with AVSG_FLAG_DENSE_MAP, every map entry -1).  This is the
+ * empty buffer that the first MTP iteration starts from (AVSG s4.4).
+ * row_mask: device int32 [B], nonzero = reset that row; NULL = all rows.
+ * Uses a kernel (no hipMemset), so it may be captured in a graph. */
 int avsg_state_init(avsg_handle* h, const int32_t* row_mask, void* stream);
 
 /* Stage One (AVSG s3.3, s3.5, s3.6 and App. B): for every request, pre-decay
@@ -254,8 +264,11 @@ int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream);
  * of the miss list.  AVSG_EINVAL if host_kv is NULL. */
 int avsg_gather(avsg_handle* h, const avsg_step_io* io, void* stream);
 
-/* avsg_match followed by avsg_gather (the gather is skipped under
- * AVSG_FLAG_SKIP_GATHER). */
+/* One recall step: avsg_match followed by avsg_gather (the gather is skipped
+ * under AVSG_FLAG_SKIP_GATHER).  This is the operator of AVSG s3.1 (Figure
+ * 2): Stage One (s3.3) resolves every selected id against the buffer as hit
+ * or miss and gives each miss a slot, then Stage Two (s3.4) fetches exactly
+ * the misses; attention then reads slot_table. */
 int avsg_step(avsg_handle* h, const avsg_step_io* io, void* stream);
 
 /* avsg_match for further query tokens of the step already begun by an
@@ -264,8 +277,14 @@ int avsg_step(avsg_handle* h, const avsg_step_io* io, void* stream);
  * avsg_match_continue on tokens B equals one avsg_match on the tokens
  * (A, B) in order whenever no cached or selected id is at or beyond the
  * verified length N (invalidation runs at the end of each call).  Used to
- * put prefetched candidates ahead of the exact selection.  AVSG_EINVAL with
- * AVSG_FLAG_SORT_MERGE (its step-local bookkeeping does not span calls). */
+ * put prefetched candidates ahead of the exact selection.  The capacity
+ * bound holds for the whole step: the handle counts the query tokens
+ * enqueued since the last avsg_match (or avsg_step), and a continuation
+ * that would bring that count times K above S returns AVSG_EINVAL without
+ * enqueuing anything (AVSG App. B, "Slot preservation": a slot referenced
+ * earlier in the step is only safe from eviction under that bound).
+ * AVSG_EINVAL with AVSG_FLAG_SORT_MERGE (its step-local bookkeeping does not
+ * span calls). */
 int avsg_match_continue(avsg_handle* h, const avsg_step_io* io, void* stream);
 
 /* Prefetch candidates (ECHO, decode prefetch: fetch during the indexer pass

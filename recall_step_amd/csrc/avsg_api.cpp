@@ -17,6 +17,7 @@ struct avsg_handle {
     int gather_blocks;
     int stage1_threads;
     int32_t* ws_pairs;        // [B][N_q][K][2] miss list when io gives none
+    int64_t step_tokens;      // query tokens enqueued since the last avsg_match
 };
 
 namespace {
@@ -94,7 +95,9 @@ int avsg_validate_config(const avsg_config* c) {
     if (c->B < 1 || c->N_q < 1 || c->K < 1 || c->K > 8192) return AVSG_EINVAL;
     if (c->S < 16 || c->S > 65536 || (c->S & (c->S - 1)) != 0) return AVSG_EINVAL;
     if (int64_t(c->N_q) * c->K > c->S) return AVSG_EINVAL;
-    if (c->L < 1 || c->L > 127 || c->R < 0) return AVSG_EINVAL;
+    // Rounds past S - 1 would only revisit buckets (odd stride, S a power
+    // of two), and the bound keeps every probe and link loop short.
+    if (c->L < 1 || c->L > 127 || c->R < 0 || c->R > c->S - 1) return AVSG_EINVAL;
     if ((c->a1 & 1u) == 0 || (c->a2 & 1u) == 0 || (c->a_fp & 1u) == 0) return AVSG_EINVAL;
     if (c->row_bytes < 16 || (c->row_bytes & 15) != 0) return AVSG_EINVAL;
     if (c->gather_blocks < 0) return AVSG_EINVAL;
@@ -212,12 +215,20 @@ int match_impl(avsg_handle* h, const avsg_step_io* io, void* stream, bool predec
 }
 
 int avsg_match(avsg_handle* h, const avsg_step_io* io, void* stream) {
-    return match_impl(h, io, stream, true);
+    int rc = match_impl(h, io, stream, true);
+    if (rc == AVSG_OK) h->step_tokens = h->cfg.N_q;
+    return rc;
 }
 
 int avsg_match_continue(avsg_handle* h, const avsg_step_io* io, void* stream) {
-    if (h && (h->cfg.flags & AVSG_FLAG_SORT_MERGE)) return AVSG_EINVAL;
-    return match_impl(h, io, stream, false);
+    if (!h || (h->cfg.flags & AVSG_FLAG_SORT_MERGE)) return AVSG_EINVAL;
+    // The capacity bound holds for the step as a whole: every query token
+    // since the step's avsg_match counts against N_q * K <= S.
+    const int64_t tokens = h->step_tokens + h->cfg.N_q;
+    if (tokens * h->cfg.K > h->cfg.S) return AVSG_EINVAL;
+    int rc = match_impl(h, io, stream, false);
+    if (rc == AVSG_OK) h->step_tokens = tokens;
+    return rc;
 }
 
 }  // extern "C"

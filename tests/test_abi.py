@@ -55,6 +55,21 @@ def test_invalid_configs_rejected(field, value):
     assert r.avsg_validate_config(c) == r.AVSG_EINVAL
 
 
+def test_probe_rounds_bounded_by_slots():
+    """R <= S - 1: with an odd stride and S a power of two the probe sequence
+    has visited every bucket after S rounds (AVSG s3.3, Probe primitive), so
+    larger R is rejected instead of running rounds that only revisit."""
+    c = r.avsg_config_default(1, 1, 16, 16, 1280)
+    for R, rc in ((0, 0), (15, 0), (16, r.AVSG_EINVAL), (2**31 - 1, r.AVSG_EINVAL)):
+        c.R = R
+        assert r.avsg_validate_config(c) == rc, R
+    c = r.avsg_config_default(1, 1, 2048, 8192, 1280)
+    c.R = 8191
+    assert r.avsg_validate_config(c) == 0
+    c.R = 8192
+    assert r.avsg_validate_config(c) == r.AVSG_EINVAL
+
+
 def test_capacity_bound_enforced():
     """N_q * K <= S (AVSG App. B slot preservation)."""
     assert r.avsg_validate_config(r.avsg_config_default(1, 4, 2048, 8192, 1280)) == 0
@@ -145,6 +160,9 @@ int main(void) {
     avsg_config_default(&c, 8, 1, 2048, 2048, 1280);
     if (avsg_validate_config(&c) != AVSG_OK) return 2;
     if (avsg_stage1_lds_bytes(&c) == 0 || avsg_workspace_bytes(&c) != 8u * 2048u * 8u) return 3;
+    c.R = c.S;
+    if (avsg_validate_config(&c) != AVSG_EINVAL) return 7;
+    c.R = 7;
     c.S = 3000;
     if (avsg_validate_config(&c) != AVSG_EINVAL) return 4;
     if (avsg_create(&c, &bufs, &h) != AVSG_EINVAL || h != NULL) return 5;

@@ -644,6 +644,44 @@ def test_prefetch_then_exact_equals_two_token_step():
         host.close()
 
 
+def test_continuation_past_the_step_capacity_is_rejected():
+    """The capacity bound N_q*K <= S (AVSG App. B, slot preservation) holds
+    for a step as a whole: a continuation that would bring the step's query
+    tokens past S/K returns AVSG_EINVAL and enqueues nothing; a new
+    avsg_match starts a new count."""
+    import torch
+    import recall_step_amd as r
+    K, S = 64, 128
+    rng = np.random.default_rng(5)
+    say("[parity] continuation capacity: B=2 K=64 S=128")
+    for Nq, continues_ok in ((1, 1), (2, 0)):
+        cfg = r.avsg_config_default(2, Nq, K, S, 16, flags=r.FLAG_SKIP_GATHER)
+        rs = r.RecallStep(cfg, None, 1000)
+        try:
+            dev = rs.Q.device
+            topk = torch.from_numpy(np.stack([
+                np.stack([rng.choice(1000, K, replace=False) for _ in range(Nq)])
+                for _ in range(2)]).astype(np.int32)).to(dev)
+            ctx = torch.full((2,), 1000, dtype=torch.int32, device=dev)
+            row_base = torch.tensor([0, 0], dtype=torch.int64, device=dev)
+            host_rows = torch.full((2,), 1000, dtype=torch.int32, device=dev)
+            io = rs.io(topk, ctx, row_base, host_rows)
+            for _ in range(2):
+                rs.match(io)
+                for _ in range(continues_ok):
+                    rs.match_continue(io)
+                torch.cuda.synchronize()
+                before = [getattr(rs, n).clone() for n in ("Q", "C", "F", "CNT")]
+                with pytest.raises(r.AvsgError) as e:
+                    rs.match_continue(io)
+                assert e.value.code == r.AVSG_EINVAL
+                torch.cuda.synchronize()
+                for n, b in zip(("Q", "C", "F", "CNT"), before):
+                    assert torch.equal(getattr(rs, n), b), n
+        finally:
+            rs.close()
+
+
 # --- dense id -> slot map matcher (ECHO page, GPU cache manager) -----------
 
 def test_dense_map_on_fuzz_corpus():
