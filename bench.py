@@ -4,11 +4,12 @@
 A step is one pass of the whole path over one batch: Stage One (probe,
 refresh, classify, allocate, link, invalidate) for every request and query
 token, then the zero-copy gather of every missed row from pinned host memory
-into the device slot buffer.  The default workload is the matching benchmark
-(batch 8, context 65536, K = 2048, S = 2048, 1280-byte rows); its seeded
-selection steps are run in order from an empty buffer (warm-up steps first,
-then the timed ones), with as many distinct steps generated as the run
-needs.
+into the device slot buffer.  The default workload is MTP-3, the largest configuration
+(batch 16, 4 query tokens per iteration through one shared buffer, context
+100000, K = 2048, S = 8192, 1280-byte rows, 131072 lookups per step); its
+32 seeded iterations are run in order from an empty buffer (warm-up steps
+first, then the timed ones), and a run asking for more than 32 is refused.
+Other workloads generate as many distinct steps as the run needs.
 
 Inputs are resident in HBM (selections) and in pinned host memory (the KV
 pool, which is where the method keeps it) before the timed region starts.
@@ -17,8 +18,9 @@ gather).  The headline step latency is the wall time of the K timed replays,
 back to back on one stream and bracketed by device synchronisation, divided
 by K; events between the replays give the per-step spread.  A first, eager
 pass with an event between the two kernels gives the per-kernel times, the
-gather bandwidth and the counters.  The CPU oracle is timed on the host
-cores beside it.
+gather bandwidth and the counters.  A third pass runs Stage One alone, its
+launches back to back between two events, for the match rate.  The CPU
+oracle is timed on the host cores beside it.
 
 Prints one JSON line.
 """
@@ -42,34 +44,38 @@ PCIE_GEN5_X16_GBPS = 64.0   # published per-direction peak of the host link
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 
 
-GATHER_PMC_SUMMARY = os.path.join(ROOT, "profiles", "gather_kernel.matching.pmc.txt")
-GATHER_SOURCES = [os.path.join(ROOT, "recall_step_amd", "csrc", f)
-                  for f in ("gather.hip", "gather.h")]
+CSRC = os.path.join(ROOT, "recall_step_amd", "csrc")
+# The sources each kernel's code comes from: a counter summary is only
+# reported while these hash to the value it was taken on.
+KERNEL_SOURCES = {"gather_kernel": ("gather.hip", "gather.h"),
+                  "stage1_kernel": ("stage_one.hip", "internal.h")}
 
 
-def gather_source_hash():
+def source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
-    for f in GATHER_SOURCES:
-        with open(f, "rb") as fh:
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(workload):
-    """HBM-side bytes per gather launch from the committed rocprofv3 PMC
-    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known
-    size), or None when the summary is for another workload or for gather
-    sources other than the ones built here."""
-    if workload != "matching" or not os.path.exists(GATHER_PMC_SUMMARY):
+def profiled_traffic(kernel, workload):
+    """HBM-side bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 PMC summary profiles/<kernel>.<workload>.pmc.txt (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what it reads for a plain copy of known size),
+    or None when there is no summary or it was taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.pmc.txt")
+    if not os.path.exists(path):
         return None
     fields = {}
-    with open(GATHER_PMC_SUMMARY) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("gather_source_sha256_16") != gather_source_hash():
+    recorded = fields.get("source_sha256_16", fields.get("gather_source_sha256_16"))
+    if recorded != source_hash(kernel):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -84,9 +90,9 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="matching",
+    ap.add_argument("--workload", default="mtp3",
                     choices=["tiny", "matching", "residency", "mtp3", "imbalanced"])
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,6 +127,12 @@ def parse():
                     help="instead of the step benchmark: Stage-One throughput on the "
                          "residency request shape (K=2048, S=8192) at B = 32..512, "
                          "one JSON line per batch size")
+    ap.add_argument("--batch", type=int, action="append",
+                    help="with --probe-sweep: only these batch sizes (repeatable)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="with --probe-sweep: end with one device copy of exactly "
+                         "1 GiB, the reference a counter run scales its byte "
+                         "counters by")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
@@ -173,11 +185,20 @@ def hbm_copy_peak(torch, stream, nbytes=1 << 30, reps=5):
     return best
 
 
+STAGE1_BYTES_MODEL = ("algorithmic bytes of the method's state accesses, wherever "
+                      "they are served: per request 2*S*4 B of lifetimes read and "
+                      "written, per lookup 9 B (id in, slot out, mask out), per bucket "
+                      "visited 8 B (word and cached id; staged in LDS here, so they do "
+                      "not reach HBM), per miss 20 B (C, F, Q install and the miss "
+                      "list entry), per token 4 B")
+
+
 def stage1_algorithmic_bytes(B, S, Nq, lookups, visits, misses):
-    """Stage-One algorithmic HBM bytes of one step: lifetimes read and written
-    once per request (2*S*4 B), 4 B id in + 4 B slot out + 1 B mask out per
-    lookup, 8 B (word + cached id) per bucket visited, 20 B per miss (install
-    12 B + miss list 8 B), 4 B count per token."""
+    """Stage-One algorithmic bytes of one step (see STAGE1_BYTES_MODEL):
+    lifetimes read and written once per request (2*S*4 B), 4 B id in + 4 B
+    slot out + 1 B mask out per lookup, 8 B (word + cached id) per bucket
+    visited, 20 B per miss (install 12 B + miss list 8 B), 4 B count per
+    token."""
     return B * 2 * S * 4 + lookups * 9 + visits * 8 + misses * 20 + B * Nq * 4
 
 
@@ -189,7 +210,7 @@ def probe_sweep(args):
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
-    for B in (32, 128, 256, 512):
+    for B in (args.batch or (32, 128, 256, 512)):
         w = make("residency", steps=40, B=B)
         cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
                                     a1=w.a1, a2=w.a2, a_fp=w.afp, flags=r.FLAG_SKIP_GATHER,
@@ -223,12 +244,15 @@ def probe_sweep(args):
             "probe_sweep": "residency request shape, Stage One only",
             "B": B, "K": w.K, "S": w.S, "stage1_us": round(us, 2),
             "match_Mkeys_per_s": round(d[r.CNT_LOOKUPS] / timed / us, 1),
-            "algorithmic_bytes_per_step": int(per_step),
+            "algorithmic_bytes_per_step": int(per_step), "bytes_model": STAGE1_BYTES_MODEL,
             "achieved_GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
             "state_traffic_GBps": round(staged / (us * 1e-6) / 1e9, 1),
             "hit_rate": round(d[r.CNT_HITS] / d[r.CNT_LOOKUPS], 4)}), flush=True)
         rs.close()
+    if args.calibration_copy:
+        log(f"[bench] calibration copy: 1 GiB device to device, "
+            f"{hbm_copy_peak(torch, stream, reps=1):.0f} GB/s")
     return 0
 
 
@@ -352,8 +376,10 @@ def ratios(args):
     """The pages' comparison points, measured in kind on this GPU:
     effective H2D bandwidth of the per-row split against request-level
     assignment (B=1, 25 % reuse) and against equal top-K partitions (B=8,
-    75 % reuse), and the recall step without reuse (KV Offload) against
-    the one with it on the matching workload."""
+    75 % reuse), all three partitions under uneven misses per request (the
+    imbalanced workload and a B=8 batch with reuse spread over 40-100 %),
+    and the recall step without reuse (KV Offload) against the one with it
+    on the matching workload."""
     import torch
     import recall_step_amd as r
     from workloads import make
@@ -377,6 +403,26 @@ def ratios(args):
             "hit_rate": res["per_row"]["hit_rate"],
             f"per_row_over_{other}": round(res["per_row"]["gather_GBps"] /
                                            res[other]["gather_GBps"], 2)}), flush=True)
+    # Uneven misses per request, where the split by missed row should matter:
+    # the imbalanced workload (64 requests, per-request miss rates 0-60 %) and
+    # 8 requests whose adjacent-step reuse spreads evenly over 40-100 %.
+    for name in ("imbalanced", "skew40to100_b8"):
+        w = make(name, steps=16)
+        host = r.HostPool(w.host_bytes)
+        w.fill_host_kv(host.array)
+        res = {p: eager_steps(r, torch, stream, w, host, f, 4, 12) for p, f in parts.items()}
+        host.close()
+        print(json.dumps({
+            "comparison": f"gather partition, {name} (B={w.B}, K={w.K}, S={w.S}, uneven "
+                          f"misses per request)",
+            "effective_GBps": {p: v["gather_GBps"] for p, v in res.items()},
+            "gather_us": {p: v["gather_us"] for p, v in res.items()},
+            "rows_per_step": res["per_row"]["rows_per_step"],
+            "hit_rate": res["per_row"]["hit_rate"],
+            "per_row_over_by_request": round(res["per_row"]["gather_GBps"] /
+                                             res["by_request"]["gather_GBps"], 2),
+            "per_row_over_by_topk": round(res["per_row"]["gather_GBps"] /
+                                          res["by_topk"]["gather_GBps"], 2)}), flush=True)
     w = make("matching")
     host = r.HostPool(w.host_bytes)
     w.fill_host_kv(host.array)
@@ -795,15 +841,20 @@ def main():
     import recall_step_amd as r
     from workloads import make
 
-    torch.cuda.set_device(0)
     # Enough distinct steps for the warm-up and the timed steps, so that no
     # selection is replayed onto a buffer that already holds it.  The MTP-3
-    # workload is defined as 32 iterations (its verified length grows into
-    # the end of the host rows), so it is replayed from its start if more
-    # steps are asked for.
+    # workload is defined as 32 iterations (its verified length grows by 4
+    # per iteration into the end of the host rows), so a run needing more is
+    # refused rather than replayed.
     need = args.warmup + args.steps
+    if args.workload == "mtp3" and need > 32:
+        print(f"bench.py: the MTP-3 workload has 32 iterations; --warmup {args.warmup} "
+              f"+ --steps {args.steps} = {need} would replay some of them onto a "
+              f"buffer that already holds them.", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
     w = make(args.workload)
-    if args.workload != "mtp3" and need > w.steps:
+    if need > w.steps:
         w = make(args.workload, steps=need)
     log(f"[bench] workload {w.name}: B={w.B} Nq={w.Nq} K={w.K} S={w.S} "
         f"row={w.row_bytes} host_bytes={w.host_bytes} steps={args.steps} warmup={args.warmup}")
@@ -882,6 +933,21 @@ def main():
     graph_wall = time.perf_counter() - tg0
     step_ms = [gev[k].elapsed_time(gev[k + 1]) for k in range(K)]
     del graphs
+
+    # Stage One alone over the same steps from an empty buffer (the gather
+    # does not change the state), its timed launches back to back between
+    # two events: the match rate without the dispatch gap that an event pair
+    # around each launch includes.
+    rs.state_init(stream=stream)
+    for t in range(args.warmup):
+        r.avsg_match(rs.handle, ios[t % w.steps], sh)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for k in range(K):
+        r.avsg_match(rs.handle, ios[(args.warmup + k) % w.steps], sh)
+    m1.record(stream)
+    torch.cuda.synchronize()
+    s1_b2b_s = m0.elapsed_time(m1) * 1e-3 / K
     d = (cnt1 - cnt0).sum(0)
     s1_ms = [e[0].elapsed_time(e[1]) for e in ev]
     g_ms = [e[1].elapsed_time(e[2]) for e in ev]
@@ -892,7 +958,7 @@ def main():
     g_avg_s = sum(g_ms) * 1e-3 / K
     step_us = graph_wall / K * 1e6
     gather_gbps = gather_bytes / (sum(g_ms) * 1e-3) / 1e9
-    mkeys = lookups / (sum(s1_ms) * 1e-3) / 1e6
+    mkeys = lookups / K / s1_b2b_s / 1e6
 
     s1_bytes_step = stage1_algorithmic_bytes(w.B, w.S, w.Nq, lookups / K, visits / K,
                                              misses / K)
@@ -921,7 +987,10 @@ def main():
         "eager_wall_us_per_step": round(wall / K * 1e6, 2),
         "gather_GBps": round(gather_gbps, 2),
         "match_Mkeys_per_s": round(mkeys, 1),
-        "stage1_us": round(s1_avg_s * 1e6, 2),
+        "match_timing": "Stage One alone, the timed launches back to back between two "
+                        "events on the launch stream; lookups per step / time per launch",
+        "stage1_us": round(s1_b2b_s * 1e6, 2),
+        "stage1_event_pair_us": round(s1_avg_s * 1e6, 2),
         "gather_us": round(g_avg_s * 1e6, 2),
         "stage1_us_p50_p90": [round(float(np.percentile(s1_ms, q)) * 1e3, 2) for q in (50, 90)],
         "gather_us_p50_p90": [round(float(np.percentile(g_ms, q)) * 1e3, 2) for q in (50, 90)],
@@ -936,18 +1005,22 @@ def main():
             "peak": PCIE_GEN5_X16_GBPS,
             "unit": "GB/s",
             "frac": round(gather_gbps / PCIE_GEN5_X16_GBPS, 4),
-            "traffic": profiled_traffic(w.name),
+            "traffic": profiled_traffic("gather_kernel", w.name),
             "kernel": "gather_kernel",
             "bytes_per_launch": round(gather_bytes / K),
+            "timing": "event pair around each launch in the eager pass, on the launch "
+                      "stream",
         },
         "roofline_stage1": {
             "bound": "hbm",
-            "achieved": round(s1_bytes_step / s1_avg_s / 1e9, 2),
+            "achieved": round(s1_bytes_step / s1_b2b_s / 1e9, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(s1_bytes_step / s1_avg_s / 1e9 / HBM_PEAK_GBPS, 5),
+            "frac": round(s1_bytes_step / s1_b2b_s / 1e9 / HBM_PEAK_GBPS, 5),
+            "traffic": profiled_traffic("stage1_kernel", w.name),
             "kernel": "stage1_kernel",
             "bytes_per_launch": round(s1_bytes_step),
+            "bytes_model": STAGE1_BYTES_MODEL,
         },
     }
 

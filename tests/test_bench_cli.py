@@ -1,8 +1,8 @@
 """The bench's host-side contract (no GPU needed): it refuses more than one
-GPU with a message, reports the profiled gather traffic only for the gather
-sources the profile was taken on, prices Stage One's algorithmic bytes by
-the unit costs it documents, and measures adjacent-step reuse by the
-page's definition."""
+GPU with a message and MTP-3 runs past its 32 iterations, reports profiled
+traffic only for the kernel sources the profile was taken on, prices Stage
+One's algorithmic bytes by the unit costs it documents, and measures
+adjacent-step reuse by the page's definition."""
 from __future__ import annotations
 
 import os
@@ -25,15 +25,25 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_profiled_traffic_follows_the_gather_sources(tmp_path, monkeypatch):
+def test_profiled_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     # The committed summary matches the committed sources.
-    assert bench.profiled_traffic("matching") is not None
-    assert bench.profiled_traffic("residency") is None
+    assert bench.profiled_traffic("gather_kernel", "matching") is not None
+    assert bench.profiled_traffic("gather_kernel", "no-such-workload") is None
     # Any change to the gather's sources makes the figure stale.
-    src = tmp_path / "gather.hip"
-    src.write_bytes(open(bench.GATHER_SOURCES[0], "rb").read() + b"\n// changed\n")
-    monkeypatch.setattr(bench, "GATHER_SOURCES", [str(src), bench.GATHER_SOURCES[1]])
-    assert bench.profiled_traffic("matching") is None
+    for f in bench.KERNEL_SOURCES["gather_kernel"]:
+        data = open(os.path.join(bench.CSRC, f), "rb").read()
+        (tmp_path / f).write_bytes(data + (b"\n// changed\n" if f.endswith(".hip") else b""))
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    assert bench.profiled_traffic("gather_kernel", "matching") is None
+
+
+def test_mtp3_runs_past_its_iterations_are_refused():
+    """MTP-3 is defined as 32 iterations from an empty buffer; the bench
+    refuses warm-up + timed steps beyond that instead of replaying."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "mtp3",
+                        "--warmup", "5", "--steps", "28"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "32 iterations" in r.stderr and r.stdout == ""
 
 
 @pytest.mark.parametrize("B,S,Nq,lookups,visits,misses", [(1, 16, 1, 0, 0, 0),

@@ -93,3 +93,12 @@ def test_fuzz_respects_the_capacity_bound():
     for seed in range(50):
         w = gen_fuzz(seed)
         assert w.Nq * w.K <= w.S and w.S in (16, 32, 64)
+
+
+def test_skewed_reuse_spans_its_range_per_request():
+    """Each request of the skewed-reuse batch keeps its own share of the
+    previous step's ids, evenly spread from 40 % to 100 %."""
+    w = make("skew40to100_b8", steps=3)
+    got = sorted(np.intersect1d(w.topk[2, b, 0], w.topk[1, b, 0]).size / w.K
+                 for b in range(w.B))
+    assert np.allclose(got, np.round(np.linspace(0.4, 1.0, w.B) * w.K) / w.K)

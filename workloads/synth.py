@@ -364,6 +364,45 @@ def gen_reuse(B, reuse, steps=16, name=None, seed=606, K=2048, S=4096):
                     np.arange(B, dtype=np.int64) * ctx)
 
 
+def gen_skewed_reuse(B=8, lo=0.4, hi=1.0, steps=16, seed=808, K=2048, S=4096):
+    """Per-request adjacent-step reuse spread over [lo, hi], so per-request
+    miss rates spread over 0-60 % as in the imbalanced workload, at the
+    matching batch of 8 (the transfer-partition comparison of the AVSG page,
+    section 4.3, where uneven misses are what a per-row split balances):
+    context 65536, K = 2048, S = 4096, 1280-B rows.
+
+    Request b keeps round(r_b * K) of its previous ids each step.  The r_b
+    are B evenly spaced values from lo to hi, in an order shuffled by
+    ``default_rng([seed, 7777])``, so a small batch spans the whole range.
+    Otherwise as ``gen_reuse``.
+    """
+    ctx = 65536
+    Nq = 1
+    reuse = np.random.default_rng([seed, 7777]).permutation(np.linspace(lo, hi, B))
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b])
+        keep = int(round(reuse[b] * K))
+        prev = None
+        for t in range(steps):
+            if prev is None:
+                ids = rng.choice(ctx, K, replace=False)
+            else:
+                kept = rng.choice(prev, keep, replace=False)
+                taken = np.zeros(ctx, bool)
+                taken[prev] = True
+                new = _take_distinct(rng, K - keep, _uniform_sampler(rng, ctx), taken)
+                ids = np.concatenate([kept, new])
+            ids = rng.permutation(ids)
+            topk[t, b, 0] = ids
+            prev = ids
+    w = Workload(f"skew{int(round(lo * 100))}to{int(round(hi * 100))}_b{B}", B, Nq, K, S,
+                 1280, steps, seed, topk, np.full((steps, B), ctx, np.int32),
+                 np.full(B, ctx, np.int32), np.arange(B, dtype=np.int64) * ctx)
+    w.extra["reuse"] = reuse
+    return w
+
+
 def stack_layers(ws, name=None):
     """One workload whose requests are the (layer, request) pairs of the
     per-layer workloads ``ws`` (same shapes): each layer keeps its own cache
@@ -432,7 +471,8 @@ def gen_reuse75_b8(steps=16):
 GENERATORS = {"tiny": gen_tiny, "matching": gen_matching,
               "residency": gen_residency, "mtp3": gen_mtp3,
               "imbalanced": gen_imbalanced, "reuse25_b1": gen_reuse25_b1,
-              "reuse75_b8": gen_reuse75_b8, "scored": gen_scored}
+              "reuse75_b8": gen_reuse75_b8, "scored": gen_scored,
+              "skew40to100_b8": gen_skewed_reuse}
 
 
 def make(name: str, **kw) -> Workload:
