@@ -49,6 +49,8 @@ extern "C" {
 #define AVSG_EHIP (-3)         /* a HIP runtime call failed */
 #define AVSG_EUNSUPPORTED (-4) /* valid for the method, beyond this build's
                                   limits (e.g. state does not fit in LDS) */
+#define AVSG_ESCRATCH (-5)     /* avsg_step_noalloc: the miss list would not
+                                  fit its static scratch */
 
 /* Per-request counters, CNT[b][0..7]; they accumulate over steps and wrap
  * modulo 2^32.  Rates are derived from them by the caller (hit rate =
@@ -307,6 +309,28 @@ int avsg_prefetch_select(avsg_handle* h, const float* scores, int64_t row_len,
  * selected.  Device pointers float [B]; 0 < alpha <= 1. */
 int avsg_ema_threshold(avsg_handle* h, const float* kth, float* theta, float alpha,
                        void* stream);
+
+/* Miss-list entries (id, slot pairs) the static scratch of
+ * avsg_step_noalloc holds on each device: 2 MiB. */
+#define AVSG_NOALLOC_MAX_PAIRS (1 << 18)
+
+/* avsg_step for callers that cannot allocate: code under HIP graph capture,
+ * serving loops that forbid hipMalloc, harnesses that own all memory.  One
+ * recall step (avsg_step's semantics and results) on the current device,
+ * with no handle: cfg and bufs are read on each call (same meaning and
+ * checks as avsg_create), io and stream as in avsg_step.  It allocates
+ * nothing, on the device or the host: when io->miss_pairs is NULL the miss
+ * list lives in a static device array of AVSG_NOALLOC_MAX_PAIRS entries that
+ * each device holds until the process ends, and a config whose
+ * B * N_q * K exceeds that returns AVSG_ESCRATCH before anything is
+ * enqueued.  The first call on a device also resolves that array's address
+ * and sets the Stage-One kernels' LDS limit there (no allocation).
+ * Every call on one device shares its array, and nothing in it needs to
+ * start cleared (each step writes the entries it reads); calls that overlap
+ * on one device, on different streams or threads, race on it, so order
+ * them, or pass io->miss_pairs.  Errors as avsg_create and avsg_step. */
+int avsg_step_noalloc(const avsg_config* cfg, const avsg_buffers* bufs,
+                      const avsg_step_io* io, void* stream);
 
 /* Allocate `bytes` of pinned host memory mapped into the device's address
  * space, suitable as host_kv; *out = host address.  Free with

@@ -34,6 +34,9 @@ AVSG_EINVAL = -1
 AVSG_ENOMEM = -2
 AVSG_EHIP = -3
 AVSG_EUNSUPPORTED = -4
+AVSG_ESCRATCH = -5
+# Miss-list entries the static scratch of avsg_step_noalloc holds per device.
+AVSG_NOALLOC_MAX_PAIRS = 1 << 18
 
 CNT_HITS, CNT_LOOKUPS, CNT_MISSES, CNT_LOST_COLLISION, CNT_LOST_EXHAUSTED, \
     CNT_LIVE_EVICTIONS, CNT_ERRORS, CNT_PROBE_VISITS = range(8)
@@ -90,6 +93,8 @@ _sigs = {
     "avsg_gather": ([_p, ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
     "avsg_step": ([_p, ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
     "avsg_match_continue": ([_p, ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
+    "avsg_step_noalloc": ([ctypes.POINTER(AvsgConfig), ctypes.POINTER(AvsgBuffers),
+                           ctypes.POINTER(AvsgStepIO), _p], ctypes.c_int),
     "avsg_prefetch_select": ([_p, _p, ctypes.c_int64, _p, _p, _p, _p, _p], ctypes.c_int),
     "avsg_ema_threshold": ([_p, _p, _p, ctypes.c_float, _p], ctypes.c_int),
     "avsg_host_alloc": ([ctypes.c_size_t, ctypes.POINTER(_p)], ctypes.c_int),
@@ -177,6 +182,11 @@ def avsg_step(h, io: AvsgStepIO, stream) -> None:
 
 def avsg_match_continue(h, io: AvsgStepIO, stream) -> None:
     _check(lib.avsg_match_continue(h, ctypes.byref(io), stream), "avsg_match_continue")
+
+
+def avsg_step_noalloc(cfg: AvsgConfig, bufs: AvsgBuffers, io: AvsgStepIO, stream) -> None:
+    _check(lib.avsg_step_noalloc(ctypes.byref(cfg), ctypes.byref(bufs), ctypes.byref(io),
+                                 stream), "avsg_step_noalloc")
 
 
 def avsg_prefetch_select(h, scores_ptr, row_len, ctx_len_ptr, theta_ptr, cap_ptr, cand_ptr,

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "avsg.h"
 #include "gather.h"
 
 namespace avsg {
@@ -172,5 +173,35 @@ hipError_t launch_ema_threshold(const EmaArgs& a, hipStream_t s);
 hipError_t sort_merge_prepare(size_t lds_bytes);
 hipError_t launch_sort_merge(const Stage1Args& a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_state_init(const InitArgs& a, hipStream_t s);
+
+// Everything a step needs besides its io: what a handle holds, or what the
+// allocation-free entry point fills in per call.
+struct StepContext {
+    avsg_config cfg;
+    avsg_buffers bufs;        // map / map_len cleared unless the dense matcher is on
+    const uint8_t* host_dev;  // device alias of bufs.host_kv (NULL without a pool)
+    size_t lds_bytes;         // Stage-One dynamic LDS of cfg
+    int gather_blocks;
+    int stage1_threads;
+    int32_t* ws_pairs;        // miss list [B][N_q][K][2] used when io->miss_pairs is NULL
+};
+
+// Records e as the thread's last HIP error and returns AVSG_EHIP.
+int hip_fail(hipError_t e);
+// Lets every Stage-One and sort-merge kernel instance use up to lds_bytes of
+// dynamic LDS on the current device.
+hipError_t prepare_kernels(size_t lds_bytes);
+// AVSG_OK if bufs suits cfg (cfg already validated), else an AVSG_E* code.
+int check_buffers(const avsg_config* cfg, const avsg_buffers* bufs);
+// Fills *out for cfg and bufs on a device with `multiprocessors` CUs and
+// `lds_limit` bytes of LDS per workgroup; resolves the host pool's device
+// alias (a lookup, no allocation).
+int fill_context(const avsg_config* cfg, const avsg_buffers* bufs, int multiprocessors,
+                 size_t lds_limit, int32_t* ws_pairs, StepContext* out);
+// Enqueue Stage One (predecay: the once-per-step decay first), Stage Two, or
+// both; each checks the io fields it reads and returns an AVSG_E* code.
+int run_match(const StepContext& x, const avsg_step_io* io, hipStream_t stream, bool predecay);
+int run_gather(const StepContext& x, const avsg_step_io* io, hipStream_t stream);
+int run_step(const StepContext& x, const avsg_step_io* io, hipStream_t stream);
 
 }  // namespace avsg

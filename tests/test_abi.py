@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strerror():
     assert r.avsg_version() == 1
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert r.avsg_strerror(code)
     assert "unknown" in r.avsg_strerror(-99)
 
@@ -68,6 +68,28 @@ def test_probe_rounds_bounded_by_slots():
     assert r.avsg_validate_config(c) == 0
     c.R = 8192
     assert r.avsg_validate_config(c) == r.AVSG_EINVAL
+
+
+def test_noalloc_step_rejects_a_miss_list_beyond_its_scratch():
+    """avsg_step_noalloc keeps the miss list in a static array of
+    AVSG_NOALLOC_MAX_PAIRS entries; a config needing more (with no
+    caller-given miss list) is refused with AVSG_ESCRATCH before any HIP
+    call or buffer access, so no GPU is needed here.  The pointers below
+    are aligned placeholders that the call must never touch."""
+    import ctypes
+    K = 2048
+    B = r.AVSG_NOALLOC_MAX_PAIRS // K + 1
+    cfg = r.avsg_config_default(B, 1, K, 4096, 1280, flags=r.FLAG_SKIP_GATHER)
+    fake = 1 << 20
+    bufs = r.AvsgBuffers(fake, fake, fake, fake, fake, None, 1000, None, 0)
+    io = r.AvsgStepIO(fake, fake, fake, fake, fake, fake, fake, None)
+    rc = r.lib.avsg_step_noalloc(ctypes.byref(cfg), ctypes.byref(bufs), ctypes.byref(io),
+                                 None)
+    assert rc == r.AVSG_ESCRATCH
+    assert "scratch" in r.avsg_strerror(rc)
+    cfg.B = 0  # an invalid config is still EINVAL, checked first
+    assert r.lib.avsg_step_noalloc(ctypes.byref(cfg), ctypes.byref(bufs), ctypes.byref(io),
+                                   None) == r.AVSG_EINVAL
 
 
 def test_capacity_bound_enforced():
