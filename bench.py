@@ -213,6 +213,11 @@ def probe_sweep(args):
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
+    # The measured HBM stream peak (a 1 GiB device copy, read plus write),
+    # beside the published one; and the counter-measured traffic of the
+    # committed summary for the batch it was taken at.
+    copy_peak = hbm_copy_peak(torch, stream)
+    counted = profiled_traffic("stage1_kernel", "probe-sweep")
     for B in (args.batch or (32, 128, 256, 512)):
         w = make("residency", steps=40, B=B)
         cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
@@ -243,15 +248,24 @@ def probe_sweep(args):
                                             d[r.CNT_MISSES] / timed)
         staged = B * (2 * 3 * w.S * 4 + w.Nq * w.K * 9)  # Q, C, F in and out + ids/outputs
         gbps = per_step / (us * 1e-6) / 1e9
-        print(json.dumps({
+        line = {
             "probe_sweep": "residency request shape, Stage One only",
             "B": B, "K": w.K, "S": w.S, "stage1_us": round(us, 2),
             "match_Mkeys_per_s": round(d[r.CNT_LOOKUPS] / timed / us, 1),
             "algorithmic_bytes_per_step": int(per_step), "bytes_model": STAGE1_BYTES_MODEL,
             "achieved_GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
             "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "measured_copy_peak_GBps": round(copy_peak, 1),
+            "frac_of_measured_peak": round(gbps / copy_peak, 4),
             "state_traffic_GBps": round(staged / (us * 1e-6) / 1e9, 1),
-            "hit_rate": round(d[r.CNT_HITS] / d[r.CNT_LOOKUPS], 4)}), flush=True)
+            "hit_rate": round(d[r.CNT_HITS] / d[r.CNT_LOOKUPS], 4)}
+        if counted is not None and B == 256:
+            cg = counted / (us * 1e-6) / 1e9
+            line["counter_traffic"] = {
+                "bytes_per_launch": counted, "source": "profiles/stage1_kernel.probe-sweep.pmc.txt",
+                "GBps": round(cg, 1), "frac": round(cg / HBM_PEAK_GBPS, 4),
+                "frac_of_measured_peak": round(cg / copy_peak, 4)}
+        print(json.dumps(line), flush=True)
         rs.close()
     if args.calibration_copy:
         log(f"[bench] calibration copy: 1 GiB device to device, "
