@@ -241,6 +241,73 @@ __device__ inline void store_outputs(int32_t* __restrict__ O, int8_t* __restrict
     }
 }
 
+// Set the bit of each miss x - base in the rank bitmap; a bit found set
+// already (a missing id that repeats) raises the flag at flag[0].
+template <int IPT>
+__device__ inline void mark_misses(uint32_t* bits, int32_t* flag, const int32_t* x,
+                                   uint32_t missm, int base, int lane) {
+    bool dup = false;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+        if (missm & (1u << e)) {
+            const uint32_t bit = uint32_t(x[e] - base);
+            const uint32_t m = 1u << (bit & 31u);
+            dup |= (atomicOr(&bits[bit >> 5], m) & m) != 0u;
+        }
+    }
+    if (__ballot(dup) != 0ull && lane == 0) flag[0] = 1;
+}
+
+// Ranks of the token's misses (ascending id) from their marks in the
+// bitmap over [idlo, idlo + 32 * nw4), nw4 a multiple of 4.  One exclusive
+// scan of the words' bit counts, which also carries the dead-slot counts of
+// the thread's lifetime words (refreshes done, installs not begun) packed
+// above them: both totals stay below 2^16 (misses <= K <= 8192, S <= 16384),
+// so the low half never carries.  If there are misses, prefix counts per
+// word (uint16, four words per step), a barrier, and one lookup per miss.
+// Returns the number of misses; every thread gets the same value.
+template <int T, int IPT>
+__device__ inline int rank_by_bitmap(const uint32_t* sBits, uint16_t* sPre, const uint32_t* sGw,
+                                     int32_t* scr, int nw4, const int32_t* x, uint32_t missm,
+                                     int idlo, int dw0, int dwn, int tid, int lane,
+                                     int32_t* rank, int* dead_pre, int* dead_all) {
+    const int wpt = ((nw4 >> 2) + T - 1) / T * 4;
+    const int w0 = min(tid * wpt, nw4), w1 = min(w0 + wpt, nw4);
+    int cnt = 0;
+    for (int k = w0; k < w1; k += 4) {
+        const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
+        cnt += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
+    }
+    int dead_local = 0;
+    for (int q = 0; q < dwn; ++q) dead_local += __popc(zero_bytes(sGw[dw0 + q]));
+    int tot;
+    int run = block_excl_scan<T>(cnt | (dead_local << 16), scr, &tot, lane);
+    *dead_pre = run >> 16;
+    *dead_all = tot >> 16;
+    const int ng = tot & 0xFFFF;
+    if (ng == 0) return 0;
+    run &= 0xFFFF;
+    for (int k = w0; k < w1; k += 4) {
+        const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
+        const uint32_t p0 = uint32_t(run);
+        const uint32_t p1 = p0 + __popc(q.x);
+        const uint32_t p2 = p1 + __popc(q.y);
+        const uint32_t p3 = p2 + __popc(q.z);
+        run = int(p3 + __popc(q.w));
+        *reinterpret_cast<uint2*>(sPre + k) = make_uint2(p0 | (p1 << 16), p2 | (p3 << 16));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+        if (missm & (1u << e)) {
+            const uint32_t bit = uint32_t(x[e] - idlo);
+            const uint32_t wd = sBits[bit >> 5];
+            rank[e] = int(sPre[bit >> 5]) + __popc(wd & ((1u << (bit & 31u)) - 1u));
+        }
+    }
+    return ng;
+}
+
 // One staging pass: int4 words j0 + u*T (u < U) of Q, C and F into LDS.
 // Branch-free so that all loads of a pass are in flight together: indices
 // past the end are clamped to the last word, and the threads that clamp
@@ -350,18 +417,27 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     const int nd = S >> 2;
     const int D = nd >= T ? nd / T : 1;  // <= 16: S <= 16384 fits LDS, T >= 256
 
-    // Counters: c_hits, c_look and c_miss are workgroup totals (the same in
-    // every thread); c_lcol, c_lexh and c_live are wave totals (from
-    // ballots); c_visit is per thread.
-    uint32_t c_hits = 0, c_look = 0, c_miss = 0;
+    // Counters: c_miss is a workgroup total (the same in every thread);
+    // c_lcol, c_lexh and c_live are wave totals (from ballots); c_look and
+    // c_visit are per thread.  Hits are lookups less misses.
+    uint32_t c_look = 0, c_miss = 0;
     uint32_t c_lcol = 0, c_lexh = 0, c_live = 0;
     uint32_t c_visit = 0, c_err = 0;
+
+    // The staging waits have returned every load issued before them.  Using
+    // the first token's ids and the old counters here tells the compiler so;
+    // otherwise the token loop's head waits for them on every token, and on
+    // later tokens that wait also drains the previous token's stores.
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) asm volatile("" ::"v"(xn[e]));
+    asm volatile("" ::"v"(cnt_old));
 
     // The rank bitmap starts every token clear: it is cleared here, while
     // the staging loads are in flight, and again after each token that used
     // it, so the rank pass needs no clear and barrier of its own.
     clear_words<T>(sBits, lay.bitmap_words, tid);
-    if (tid == 0) sMisc[0] = 0;  // repeated-id flag
+    if (tid == 0) sMisc[0] = 0;      // repeated-id flag
+    if (tid < 8) sMisc[2 + tid] = 0;  // the counters' workgroup sums, taken at the end
     __syncthreads();
 
     // N_q >= 1: a do-while leaves no path on which the loop body is skipped,
@@ -483,24 +559,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         }
         const int m_local = __popc(missm);
 
-        // Miss and valid-id totals in one sum (each at most K < 2^16).  When
-        // the request's rows fit the rank bitmap, the bitmap spans [0,
-        // host_rows) (every valid id is below it) and the id range is not
-        // reduced.
-        int nsum, idlo, idhi;
-        if (narrow_rows) {
-            nsum = block_sum<T>(m_local | (__popc(valid) << 16), sMM, lane_t);
-            idlo = 0;
-            idhi = hr - 1;
-        } else {
-            block_sum_min_max<T>(m_local | (__popc(valid) << 16), lo_local, hi_local, sMM, &nsum,
-                                 &idlo, &idhi, lane_t);
-        }
-        const int ng = min(nsum & 0xFFFF, K);
-        const int nvalid = nsum >> 16;
-        c_look += uint32_t(nvalid);
-        c_hits += uint32_t(nvalid - ng);
-        c_miss += uint32_t(ng);
+        c_look += uint32_t(__popc(valid));
 
         // --- Rank of each miss among the token's misses, ascending id ------
         int32_t rank[IPT];
@@ -509,90 +568,69 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         // Dead-slot prefix and total, when the rank scan counted them (-1:
         // not counted).
         int dead_pre = -1, dead_all = -1;
-        if (ng > 0) {
-            const uint32_t span = uint32_t(idhi) - uint32_t(idlo) + 1u;  // ids >= 0
-            bool fast = span <= uint32_t(lay.bitmap_words) * 32u;
-            if (fast) {
-                const int nw4 = int(((span + 31u) >> 5) + 3) & ~3;  // words, multiple of 4
-                bool dup = false;
-#pragma unroll
-                for (int e = 0; e < IPT; ++e) {
-                    if (missm & (1u << e)) {
-                        const uint32_t bit = uint32_t(x[e] - idlo);
-                        const uint32_t m = 1u << (bit & 31u);
-                        dup |= (atomicOr(&sBits[bit >> 5], m) & m) != 0u;
-                    }
-                }
-                if (__ballot(dup) != 0ull && lane_t == 0) sMisc[0] = 1;
-                __syncthreads();
-                fast = sMisc[0] == 0;
-                if (fast) {
-                    // Prefix popcounts over the words, as uint16 (ng <= 8192),
-                    // four words per step.  The same scan also takes the
-                    // dead-slot counts of the victim pass (refreshes are
-                    // done, installs not begun), packed above the bit counts:
-                    // both totals stay below 2^16 (ng <= K <= 8192, S <=
-                    // 16384), so the low half never carries.
-                    const int wpt = ((nw4 >> 2) + T - 1) / T * 4;
-                    const int w0 = min(tid_t * wpt, nw4), w1 = min(w0 + wpt, nw4);
-                    int cnt = 0;
-                    for (int k = w0; k < w1; k += 4) {
-                        const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
-                        cnt += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
-                    }
-                    int dead_local = 0;
-                    for (int q = 0; q < dwn_t; ++q)
-                        dead_local += __popc(zero_bytes(sGw[dw0_t + q]));
-                    int tot;
-                    int run = block_excl_scan<T>(cnt | (dead_local << 16), sS0, &tot, lane_t);
-                    dead_pre = run >> 16;
-                    dead_all = tot >> 16;
-                    run &= 0xFFFF;
-                    for (int k = w0; k < w1; k += 4) {
-                        const uint4 q = *reinterpret_cast<const uint4*>(sBits + k);
-                        const uint32_t p0 = uint32_t(run);
-                        const uint32_t p1 = p0 + __popc(q.x);
-                        const uint32_t p2 = p1 + __popc(q.y);
-                        const uint32_t p3 = p2 + __popc(q.z);
-                        run = int(p3 + __popc(q.w));
-                        *reinterpret_cast<uint2*>(sPre + k) =
-                            make_uint2(p0 | (p1 << 16), p2 | (p3 << 16));
-                    }
-                    __syncthreads();
-#pragma unroll
-                    for (int e = 0; e < IPT; ++e) {
-                        if (missm & (1u << e)) {
-                            const uint32_t bit = uint32_t(x[e] - idlo);
-                            const uint32_t wd = sBits[bit >> 5];
-                            rank[e] = int(sPre[bit >> 5]) +
-                                      __popc(wd & ((1u << (bit & 31u)) - 1u));
-                        }
-                    }
-                }
+        int ng = 0;
+        bool sorted_rank = false;  // the general-order sort ranks the misses
+        if (!DENSE && narrow_rows) {
+            // The bitmap spans [0, host_rows), which holds every valid id:
+            // the misses are marked at once, and after one barrier the rank
+            // scan also yields their count.  (The dense matcher clears the
+            // bitmap at the token's start with no barrier before this point,
+            // so it takes the other branch.)
+            mark_misses<IPT>(sBits, sMisc, x, missm, 0, lane_t);
+            __syncthreads();
+            if (sMisc[0] == 0) {
+                const int nw4 = int(((uint32_t(hr) + 31u) >> 5) + 3) & ~3;
+                ng = rank_by_bitmap<T, IPT>(sBits, sPre, sGw, sS0, nw4, x, missm, 0, dw0_t,
+                                            dwn_t, tid_t, lane_t, rank, &dead_pre, &dead_all);
+            } else {
+                sorted_rank = true;  // a missing id repeats
             }
-            if (!fast) {
-                // General order: bitonic sort of (id << 16 | position) keys.
-                int tot;
-                int off = block_excl_scan<T>(m_local, sS1, &tot, lane_t);
-#pragma unroll
-                for (int e = 0; e < IPT; ++e)
-                    if (missm & (1u << e))
-                        sKey[off++] = (uint64_t(uint32_t(x[e])) << 16) | uint64_t(i0_t + e);
-                const int P = next_pow2(ng);
-                for (int r = ng + tid_t; r < P; r += T) sKey[r] = ~uint64_t(0);
-                __syncthreads();
-                bitonic_sort<T>(sKey, P);
-                for (int r = tid_t; r < ng; r += T) {
-                    const uint64_t k = sKey[r];
-                    sRank[int(k & 0xFFFFu)] = uint16_t(r);
-                    if (r + 1 < ng && (k >> 16) == (sKey[r + 1] >> 16)) c_err |= 2u;
+        } else {
+            // Miss count (at most K < 2^16) and, unless the bitmap spans the
+            // request's rows, the id range of the misses.
+            int idlo = 0, idhi = hr - 1;
+            if (narrow_rows)
+                ng = block_sum<T>(m_local, sMM, lane_t);
+            else
+                block_sum_min_max<T>(m_local, lo_local, hi_local, sMM, &ng, &idlo, &idhi, lane_t);
+            if (ng > 0) {
+                const uint32_t span = uint32_t(idhi) - uint32_t(idlo) + 1u;  // ids >= 0
+                sorted_rank = span > uint32_t(lay.bitmap_words) * 32u;
+                if (!sorted_rank) {
+                    mark_misses<IPT>(sBits, sMisc, x, missm, idlo, lane_t);
+                    __syncthreads();
+                    sorted_rank = sMisc[0] != 0;
+                    if (!sorted_rank) {
+                        const int nw4 = int(((span + 31u) >> 5) + 3) & ~3;
+                        rank_by_bitmap<T, IPT>(sBits, sPre, sGw, sS0, nw4, x, missm, idlo, dw0_t,
+                                               dwn_t, tid_t, lane_t, rank, &dead_pre, &dead_all);
+                    }
                 }
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < IPT; ++e)
-                    if (missm & (1u << e)) rank[e] = int(sRank[i0_t + e]);
             }
         }
+        if (sorted_rank) {
+            // General order: bitonic sort of (id << 16 | position) keys.  The
+            // scan that places the keys also counts the misses.
+            int off = block_excl_scan<T>(m_local, sS1, &ng, lane_t);
+#pragma unroll
+            for (int e = 0; e < IPT; ++e)
+                if (missm & (1u << e))
+                    sKey[off++] = (uint64_t(uint32_t(x[e])) << 16) | uint64_t(i0_t + e);
+            const int P = next_pow2(ng);
+            for (int r = ng + tid_t; r < P; r += T) sKey[r] = ~uint64_t(0);
+            __syncthreads();
+            bitonic_sort<T>(sKey, P);
+            for (int r = tid_t; r < ng; r += T) {
+                const uint64_t k = sKey[r];
+                sRank[int(k & 0xFFFFu)] = uint16_t(r);
+                if (r + 1 < ng && (k >> 16) == (sKey[r + 1] >> 16)) c_err |= 2u;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < IPT; ++e)
+                if (missm & (1u << e)) rank[e] = int(sRank[i0_t + e]);
+        }
+        c_miss += uint32_t(ng);
 
         if (ng > 0) {
             // --- Pass 3: victims ---------------------------------------------
@@ -791,7 +829,11 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         if (tid_t == 0) a.n_miss[tok] = ng;
         if (ng > 0 && tid_t == 0) sMisc[0] = 0;  // read before two barriers at least
         if constexpr (DENSE) region_dirty = ng > 0;
-        __syncthreads();
+        // The end of the step reads C and the lifetimes, whose last writes
+        // (refreshes, decay, installs) came before a barrier of this token,
+        // so only a following token (or the dense matcher's map updates)
+        // needs this one.
+        if (DENSE || g + 1 < a.Nq) __syncthreads();
     } while (++g < a.Nq);
 
     // End of step: empty every slot caching a speculative id (>= N) and
@@ -815,13 +857,13 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     }
 
     // Counters: one wave sum (visits), then one LDS atomic per wave for
-    // each counter kept per wave.
+    // each counter kept per wave, into sums zeroed before the first token.
     int32_t* sCnt = sMisc + 2;
-    if (tid < 8) sCnt[tid] = 0;
-    __syncthreads();
     const int visits = lane63(wave_scan_add(int(c_visit)));
+    const int looks = lane63(wave_scan_add(int(c_look)));
     const uint64_t e1 = __ballot(c_err & 1u), e2 = __ballot(c_err & 2u);
     if (lane == 0) {
+        if (looks) atomicAdd(&sCnt[1], looks);
         if (c_lcol) atomicAdd(&sCnt[3], int(c_lcol));
         if (c_lexh) atomicAdd(&sCnt[4], int(c_lexh));
         if (c_live) atomicAdd(&sCnt[5], int(c_live));
@@ -831,8 +873,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     __syncthreads();
     if (tid < 8) {
         int32_t* cnt = a.CNT + size_t(b) * 8;
-        const uint32_t add = tid == 0   ? c_hits
-                             : tid == 1 ? c_look
+        const uint32_t add = tid == 0   ? uint32_t(sCnt[1]) - c_miss
                              : tid == 2 ? c_miss
                                         : uint32_t(sCnt[tid]);
         if (tid == 6)
