@@ -762,6 +762,20 @@ def contiguous_gather_peak(r, torch, stream, row_bytes=1280, rows=1 << 19, block
     return best
 
 
+def host_cpu_model():
+    """The host CPU's model name and logical CPU count, as the OS reports them."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs visible"
+
+
 def cpu_baseline(w, host_array, warmup, steps, budget_s):
     """The CPU oracle as it stands, single thread, on the same steps."""
     import oracle
@@ -1080,16 +1094,18 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the same steps")
         per_step, passes = cpu_baseline(w, host.array, args.warmup, K, args.cpu_seconds)
+        cpu = host_cpu_model()
         result["cpu_baseline"] = {
             "value": round(per_step * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
             "sample": f"{w.name} workload, full batch, the same {K} timed steps after "
                       f"{args.warmup} warm-up steps, {passes} passes from an empty "
                       f"buffer, median per-step time (single thread, gcc -O2)",
+            "cpu": cpu,
         }
         per_step_mt, threads = cpu_baseline_all_cores(w, host.array, args.warmup, K)
         result["cpu_baseline_all_cores"] = {
             "value": round(per_step_mt * 1e6, 1), "unit": "us", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu,
             "sample": f"{w.name} workload, the same {K} timed steps after {args.warmup} "
                       f"warm-up steps, one pass from an empty buffer; each request in its "
                       f"own single-request oracle, requests spread over {threads} threads",
