@@ -89,6 +89,7 @@ int fill_context(const avsg_config* cfg, const avsg_buffers* bufs, int multiproc
     out->lds_bytes = lds;
     out->gather_blocks = cfg->gather_blocks > 0 ? cfg->gather_blocks : multiprocessors;
     out->stage1_threads = stage1_threads(cfg->K, cfg->stage1_threads);
+    out->stage1_grid = multiprocessors > 0 ? multiprocessors : 1;
     out->ws_pairs = ws_pairs;
     return AVSG_OK;
 }
@@ -143,7 +144,7 @@ int run_match(const StepContext& x, const avsg_step_io* io, hipStream_t stream,
     a.map_len = x.bufs.map_len;
     hipError_t e = (c.flags & AVSG_FLAG_SORT_MERGE)
                        ? launch_sort_merge(a, x.lds_bytes, stream)
-                       : launch_stage1(a, x.stage1_threads, x.lds_bytes,
+                       : launch_stage1(a, x.stage1_threads, x.stage1_grid, x.lds_bytes,
                                        (c.flags & AVSG_FLAG_DENSE_MAP) != 0, stream);
     return e == hipSuccess ? AVSG_OK : hip_fail(e);
 }

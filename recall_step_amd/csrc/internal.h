@@ -148,8 +148,10 @@ struct InitArgs {
 int stage1_threads(int K, int requested);
 hipError_t stage1_prepare(size_t lds_bytes);
 // dense: match through the id -> slot map instead of the hash table.
-hipError_t launch_stage1(const Stage1Args& a, int threads, size_t lds_bytes, bool dense,
-                         hipStream_t s);
+// grid: the most workgroups to launch (one per CU); with more requests than
+// that, the hash matcher's workgroups each take several in turn.
+hipError_t launch_stage1(const Stage1Args& a, int threads, int grid, size_t lds_bytes,
+                         bool dense, hipStream_t s);
 struct PrefetchArgs {
     const float* __restrict__ scores;  // [B][row_len]
     int64_t row_len;
@@ -183,6 +185,7 @@ struct StepContext {
     size_t lds_bytes;         // Stage-One dynamic LDS of cfg
     int gather_blocks;
     int stage1_threads;
+    int stage1_grid;          // most Stage-One workgroups: one per CU
     int32_t* ws_pairs;        // miss list [B][N_q][K][2] used when io->miss_pairs is NULL
 };
 
