@@ -66,6 +66,38 @@ def test_more_requests_than_cus_at_the_largest_state():
     assert cnt[:, 5].sum() > 0  # live evictions: the buffers did fill
 
 
+@pytest.mark.parametrize("K,S,threads", [(4096, 8192, 0), (1000, 1024, 256), (256, 512, 0),
+                                         (2048, 8192, 512), (256, 16384, 0)])
+def test_more_requests_than_cus_every_form(K, S, threads):
+    """300 requests, more than the 256 CUs, so each workgroup takes several.
+    The next request is loaded ahead with two state words per array per
+    thread (K = 4096: four ids per thread) or one (S = 1024 at 256 threads;
+    S = 512 with one id per thread); past two words (S = 8192 at 512
+    threads, S = 16384 at 256) it is staged from memory.  Half of each
+    selection carries over, so hits, refreshes and evictions all occur."""
+    prev = {}
+
+    def draw(rng, t, b):
+        if b in prev:
+            keep = rng.choice(prev[b], K // 2, replace=False)
+            fresh = np.setdiff1d(rng.choice(3 * K, 2 * K, replace=False), keep)[: K - keep.size]
+            ids = np.concatenate([keep, fresh])
+        else:
+            ids = rng.choice(3 * K, K, replace=False)
+        prev[b] = ids
+        return rng.permutation(ids).astype(np.int32)
+
+    w = _stage_one_only(f"B=300 K={K} S={S}", K, S, 6, 300, 4 * K, draw)
+    cnt = run_parity(w, gather=False, stage1_threads=threads)
+    assert cnt[:, 0].sum() > 0 and cnt[:, 2].sum() > 0  # hits and misses
+
+
+def test_more_requests_than_cus_with_query_tokens():
+    """MTP-3 requests, 300 of them: the last query token of one request loads
+    the next request's first ids, and invalidation runs per request."""
+    run_parity(make("mtp3", steps=4, B=300), gather=False, label="mtp3 B=300")
+
+
 @pytest.mark.parametrize("K,S", [(256, 512), (1000, 1024), (2048, 2048), (3000, 4096),
                                  (4096, 8192), (1, 16), (64, 64), (1501, 2048),
                                  (2999, 4096), (4095, 8192), (256, 16384), (1023, 16384)])
