@@ -128,7 +128,7 @@ def parse():
                          "of the residency shape against the lifetime L")
     ap.add_argument("--probe-sweep", action="store_true",
                     help="instead of the step benchmark: Stage-One throughput on the "
-                         "residency request shape (K=2048, S=8192) at B = 32..512, "
+                         "residency request shape (K=2048, S=8192) at B = 32..1024, "
                          "one JSON line per batch size")
     ap.add_argument("--batch", type=int, action="append",
                     help="with --probe-sweep: only these batch sizes (repeatable)")
@@ -218,7 +218,7 @@ def probe_sweep(args):
     # committed summary for the batch it was taken at.
     copy_peak = hbm_copy_peak(torch, stream)
     counted = profiled_traffic("stage1_kernel", "probe-sweep")
-    for B in (args.batch or (32, 128, 256, 512)):
+    for B in (args.batch or (32, 128, 256, 512, 1024)):
         w = make("residency", steps=40, B=B)
         cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
                                     a1=w.a1, a2=w.a2, a_fp=w.afp, flags=r.FLAG_SKIP_GATHER,
