@@ -7,9 +7,11 @@
 // sequence through one buffer) and Appendix B (single packed-word scatter,
 // exhausted probes, slot preservation, speculative invalidation).
 //
-// gfx950 mapping.  One workgroup owns one request for the whole step.  Its
-// bucket words and cached ids (int32) and its lifetimes are staged in LDS
-// once and every query token runs against the LDS copy.  Installs and links
+// gfx950 mapping.  One workgroup owns one request for the whole step (with
+// more requests than CUs, one workgroup per CU takes several in turn, the
+// next one's state loaded into registers while it works on the current).
+// Its bucket words and cached ids (int32) and its lifetimes are staged in
+// LDS once and every query token runs against the LDS copy.  Installs and links
 // write their C and Q entries through to global memory as they happen, so
 // the end of the step writes back only the lifetimes and the slots it
 // empties.  Lifetimes are held as one byte per slot, G = F + 1 (0 = dead,
@@ -29,11 +31,12 @@
 // slot-table and hit-mask entries with vector stores.  The install leaves the
 // misses in rank order in LDS, and the link runs over that list, one miss per
 // lane, so only as many waves as there are misses walk its rounds.  The rank
-// comes from a bitmap over [min id, max id] of the
-// token's misses held in LDS: one atomicOr per miss, then prefix popcounts
-// over the words, so rank(x) = (misses below x's word) + popc(word bits below
-// x).  When the ids span more than the bitmap or a missing id repeats, the
-// token falls back to a bitonic sort of (id, position) keys in LDS.
+// comes from a bitmap held in LDS over [0, host rows) of the request (or, if
+// those do not fit it, over [min id, max id] of the token's misses): one
+// atomicOr per miss, then prefix popcounts over the words, so rank(x) =
+// (misses below x's word) + popc(word bits below x); the same scan counts
+// the misses.  When the ids span more than the bitmap or a missing id
+// repeats, the token falls back to a bitonic sort of (id, position) keys.
 //
 // Victims: the dead-slot count is an exclusive scan over slots in index
 // order; only when it is short of the miss count does the workgroup build a
