@@ -63,11 +63,12 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(kernel, workload):
+def profiled_traffic(kernel, workload, key="traffic_bytes_per_launch"):
     """HBM-side bytes per launch of `kernel` on `workload` from the committed
     rocprofv3 PMC summary profiles/<kernel>.<workload>.pmc.txt (FETCH_SIZE and
     WRITE_SIZE, each scaled by what it reads for a plain copy of known size),
-    or None when there is no summary or it was taken on other sources."""
+    or None when there is no summary or it was taken on other sources.  `key`
+    names the figure (the probe sweep's summary holds one per batch size)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.pmc.txt")
     if not os.path.exists(path):
         return None
@@ -81,7 +82,7 @@ def profiled_traffic(kernel, workload):
     if recorded != source_hash(kernel):
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[key])
     except (KeyError, ValueError):
         return None
 
@@ -215,10 +216,11 @@ def probe_sweep(args):
     sh = stream.cuda_stream
     # The measured HBM stream peak (a 1 GiB device copy, read plus write),
     # beside the published one; and the counter-measured traffic of the
-    # committed summary for the batch it was taken at.
+    # committed summary at each batch size it holds.
     copy_peak = hbm_copy_peak(torch, stream)
-    counted = profiled_traffic("stage1_kernel", "probe-sweep")
     for B in (args.batch or (32, 128, 256, 512, 1024)):
+        counted = profiled_traffic("stage1_kernel", "probe-sweep",
+                                   f"traffic_bytes_per_launch_B{B}")
         w = make("residency", steps=40, B=B)
         cfg = r.avsg_config_default(w.B, w.Nq, w.K, w.S, w.row_bytes, L=w.L, R=w.R,
                                     a1=w.a1, a2=w.a2, a_fp=w.afp, flags=r.FLAG_SKIP_GATHER,
@@ -259,7 +261,7 @@ def probe_sweep(args):
             "frac_of_measured_peak": round(gbps / copy_peak, 4),
             "state_traffic_GBps": round(staged / (us * 1e-6) / 1e9, 1),
             "hit_rate": round(d[r.CNT_HITS] / d[r.CNT_LOOKUPS], 4)}
-        if counted is not None and B == 256:
+        if counted is not None:
             cg = counted / (us * 1e-6) / 1e9
             line["counter_traffic"] = {
                 "bytes_per_launch": counted, "source": "profiles/stage1_kernel.probe-sweep.pmc.txt",

@@ -37,6 +37,21 @@ def test_profiled_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.profiled_traffic("gather_kernel", "matching") is None
 
 
+def test_probe_sweep_counters_cover_every_batch_size():
+    """The committed sweep summary holds counter bytes for each batch size the
+    sweep runs, growing with the batch, and its B = 256 figure agrees with
+    the separate B = 256 run."""
+    per_b = [bench.profiled_traffic("stage1_kernel", "probe-sweep",
+                                    f"traffic_bytes_per_launch_B{B}")
+             for B in (32, 128, 256, 512, 1024)]
+    assert all(v is not None for v in per_b)
+    assert per_b == sorted(per_b)
+    single = bench.profiled_traffic("stage1_kernel", "probe-sweep")
+    assert abs(per_b[2] - single) <= 1e-3 * single
+    assert bench.profiled_traffic("stage1_kernel", "probe-sweep",
+                                  "traffic_bytes_per_launch_B7") is None
+
+
 def test_mtp3_runs_past_its_iterations_are_refused():
     """MTP-3 is defined as 32 iterations from an empty buffer; the bench
     refuses warm-up + timed steps beyond that instead of replaying."""
