@@ -320,6 +320,42 @@ __device__ inline uint32_t lifetime_word(int4 f, int gadd, int L) {
     return g0 | (g1 << 8) | (g2 << 16) | (g3 << 24);
 }
 
+// Link rounds over the first NE of a thread's IPT misses: the first
+// reusable bucket (empty, its slot empty, or its fingerprint not the slot's
+// id's) in R+1 rounds, judged on the bucket words before this token's link
+// writes.  Branch-free within a round; a wave leaves once none of its
+// misses still searches.  A round's time is one wave's chain of dependent
+// instructions, so a wave whose lanes search with their first NE ids only
+// (ranks tid + e*T, e < NE; with at most T misses in a token, NE = 1 in
+// every wave) walks the rounds over those, keeping the other ids' reads and
+// tests out of the chain.
+template <int NE, int IPT>
+__device__ inline void link_rounds(const int32_t* sQ, const int32_t* sC, uint32_t (&lp)[IPT],
+                                   const uint32_t (&ld)[IPT], int32_t (&tgt)[IPT],
+                                   uint32_t& search, int R, uint32_t smask, uint32_t afp) {
+    for (int t = 0; t <= R; ++t) {
+        if (__ballot(search != 0u) == 0ull) break;
+        int32_t wd[NE], cc[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) wd[e] = sQ[((search >> e) & 1u) ? lp[e] : 0u];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
+        uint32_t takem = 0;
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            takem |= uint32_t((wd[e] == kEmpty) | (cc[e] == -1) |
+                              (fp_of(uint32_t(cc[e]), afp) != (wd[e] >> 16)))
+                     << e;
+        takem &= search;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            tgt[e] = ((takem >> e) & 1u) ? int32_t(lp[e]) : tgt[e];
+            lp[e] = (lp[e] + ld[e]) & smask;
+        }
+        search &= ~takem;
+    }
+}
+
 // One staging pass: int4 words j0 + u*T (u < U) of Q, C and F into LDS.
 // Branch-free so that all loads of a pass are in flight together: indices
 // past the end are clamped to the last word, and the threads that clamp
@@ -837,28 +873,23 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     #pragma unroll
                     for (int e = 0; e < IPT; ++e)
                         if ((search >> e) & 1u) P[tid_t + e * T] = make_int2(lx[e], ls[e]);
-                    // Checked every round: most links succeed in the first.
-                    for (int t = 0; t <= R; ++t) {
-                        if (__ballot(search != 0u) == 0ull) break;
-                        int32_t wd[IPT], cc[IPT];
+                    // Checked every round: most links succeed in the first.  The
+                    // wave walks the rounds over as many ids per lane as its
+                    // lanes' highest searching id needs (1, 2, 4 or IPT).
+                    uint32_t wave_ids = 0;
     #pragma unroll
-                        for (int e = 0; e < IPT; ++e) wd[e] = sQ[((search >> e) & 1u) ? lp[e] : 0u];
-    #pragma unroll
-                        for (int e = 0; e < IPT; ++e) cc[e] = sC[wd[e] & int32_t(smask)];
-                        uint32_t takem = 0;
-    #pragma unroll
-                        for (int e = 0; e < IPT; ++e)
-                            takem |= uint32_t((wd[e] == kEmpty) | (cc[e] == -1) |
-                                              (fp_of(uint32_t(cc[e]), a.afp) != (wd[e] >> 16)))
-                                     << e;
-                        takem &= search;
-    #pragma unroll
-                        for (int e = 0; e < IPT; ++e) {
-                            tgt[e] = ((takem >> e) & 1u) ? int32_t(lp[e]) : tgt[e];
-                            lp[e] = (lp[e] + ld[e]) & smask;
-                        }
-                        search &= ~takem;
-                    }
+                    for (int e = 1; e < IPT; ++e)
+                        wave_ids |= uint32_t(__ballot((search >> e) & 1u) != 0ull) << e;
+                    if (wave_ids == 0u)
+                        link_rounds<1, IPT>(sQ, sC, lp, ld, tgt, search, R, smask, a.afp);
+                    else if (IPT >= 4 && wave_ids < 4u)
+                        link_rounds<(IPT >= 4 ? 2 : 1), IPT>(sQ, sC, lp, ld, tgt, search, R,
+                                                            smask, a.afp);
+                    else if (IPT >= 8 && wave_ids < 16u)
+                        link_rounds<(IPT >= 8 ? 4 : 1), IPT>(sQ, sC, lp, ld, tgt, search, R,
+                                                            smask, a.afp);
+                    else
+                        link_rounds<IPT, IPT>(sQ, sC, lp, ld, tgt, search, R, smask, a.afp);
     #pragma unroll
                     for (int e = 0; e < IPT; ++e)
                         c_lexh += uint32_t(__popcll(__ballot((search >> e) & 1u)));
