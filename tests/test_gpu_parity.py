@@ -826,3 +826,68 @@ def test_dense_map_continuation_equals_two_token_step():
     finally:
         rs.close()
         host.close()
+
+
+@pytest.mark.parametrize("K,S", [(2048, 8192), (1000, 4096)])
+def test_continuation_with_more_requests_than_cus(K, S):
+    """300 requests, more than the CUs, so each workgroup takes several and
+    loads the next one's state ahead, here without the once-per-step decay
+    in the continuation: a match on token A then avsg_match_continue on
+    token B equal the oracle's one step over (A, B), outputs of both calls,
+    state and counters.  No id is at or beyond the verified length, so the
+    invalidation at the end of the first call changes nothing."""
+    import torch
+    import recall_step_amd as r
+    from oracle import Oracle
+    B, hr, steps = 300, 4 * K, 4
+    rng = np.random.default_rng([K, S, 300])
+    toks = np.full((steps, B, 2, K), -1, np.int32)
+    prev = [None] * B
+    for t in range(steps):
+        for b in range(B):
+            for g in range(2):
+                if prev[b] is not None:
+                    keep = rng.choice(prev[b], K // 2, replace=False)
+                    fresh = np.setdiff1d(rng.choice(hr, 2 * K, replace=False), keep)[: K - K // 2]
+                    ids = np.concatenate([keep, fresh])
+                else:
+                    ids = rng.choice(hr, K, replace=False)
+                prev[b] = ids
+                toks[t, b, g] = rng.permutation(ids)
+    say(f"[parity] continuation B=300 K={K} S={S}")
+    cfg = r.avsg_config_default(B, 1, K, S, 16, flags=r.FLAG_SKIP_GATHER)
+    rs = r.RecallStep(cfg, None, B * hr)
+    o = Oracle(B, 2, K, S, cfg.L, cfg.R, cfg.a1, cfg.a2, cfg.a_fp, 16, B * hr, shadow=False)
+    dev = rs.Q.device
+    try:
+        ctx = torch.full((B,), hr, dtype=torch.int32, device=dev)
+        row_base = torch.arange(B, dtype=torch.int64, device=dev) * hr
+        host_rows = torch.full((B,), hr, dtype=torch.int32, device=dev)
+        out1 = [torch.empty_like(x) for x in (rs.slot_table, rs.hit_mask, rs.n_miss,
+                                              rs.miss_pairs)]
+        for t in range(steps):
+            ta = torch.from_numpy(np.ascontiguousarray(toks[t, :, :1])).to(dev)
+            tb = torch.from_numpy(np.ascontiguousarray(toks[t, :, 1:])).to(dev)
+            io1 = r.AvsgStepIO(ta.data_ptr(), ctx.data_ptr(), row_base.data_ptr(),
+                               host_rows.data_ptr(), out1[0].data_ptr(), out1[1].data_ptr(),
+                               out1[2].data_ptr(), out1[3].data_ptr())
+            rs.match(io1)
+            rs.match_continue(rs.io(tb, ctx, row_base, host_rows))
+            torch.cuda.synchronize()
+            ref = o.step(toks[t], np.full(B, hr, np.int32), np.arange(B, dtype=np.int64) * hr,
+                         np.full(B, hr, np.int32))
+            for g, outs in ((0, [x.cpu().numpy() for x in out1]),
+                            (1, [x.cpu().numpy() for x in (rs.slot_table, rs.hit_mask,
+                                                           rs.n_miss, rs.miss_pairs)])):
+                assert np.array_equal(outs[0][:, 0], ref.slot_table[:, g]), f"{t}/{g} slots"
+                assert np.array_equal(outs[1][:, 0], ref.hit_mask[:, g]), f"{t}/{g} mask"
+                assert np.array_equal(outs[2][:, 0], ref.n_miss[:, g]), f"{t}/{g} n"
+                for b in range(B):
+                    n = int(ref.n_miss[b, g])
+                    assert np.array_equal(outs[3][b, 0, :n], ref.miss_pairs[b, g, :n]), \
+                        f"{t}/{g} miss list of request {b}"
+            for name in ("Q", "C", "F", "CNT"):
+                assert np.array_equal(getattr(rs, name).cpu().numpy(), getattr(o, name)), name
+        assert int(o.CNT[:, 0].sum()) > 0 and int(o.CNT[:, 2].sum()) > 0  # hits and misses
+    finally:
+        rs.close()
