@@ -10,7 +10,7 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
-from workloads import gen_fuzz, make
+from workloads import gen_fuzz, gen_medium, make
 
 
 def adjacent_reuse(w, g=0):
@@ -102,3 +102,26 @@ def test_skewed_reuse_spans_its_range_per_request():
     got = sorted(np.intersect1d(w.topk[2, b, 0], w.topk[1, b, 0]).size / w.K
                  for b in range(w.B))
     assert np.allclose(got, np.round(np.linspace(0.4, 1.0, w.B) * w.K) / w.K)
+
+
+def test_medium_cases_are_reproducible_and_within_bounds():
+    """The random medium cases: a pure function of the seed, within the
+    capacity bound and the supported sizes, distinct ids per token apart
+    from padding, and ids of each token inside the request's rows except
+    the planted out-of-range ones."""
+    for seed in range(32):
+        w, w2 = gen_medium(seed), gen_medium(seed)
+        assert np.array_equal(w.topk, w2.topk) and np.array_equal(w.ctx_len, w2.ctx_len)
+        assert 1 <= w.K <= 4096 and 1 <= w.Nq <= 4 and w.Nq * w.K <= min(w.S, 8192)
+        assert w.S & (w.S - 1) == 0 and 16 <= w.S <= 16384 and 1 <= w.B <= 300
+        assert w.topk.shape == (w.steps, w.B, w.Nq, w.K)
+        for t in range(w.steps):
+            for b in range(w.B):
+                hr = int(w.host_rows[b])
+                assert 1 <= w.ctx_len[t, b] <= hr
+                for g in range(w.Nq):
+                    row = w.topk[t, b, g]
+                    ids = row[(row >= 0) & (row < hr)]
+                    assert np.unique(ids).size == ids.size
+                    planted = row[(row != -1) & ((row < 0) | (row >= hr))]
+                    assert planted.size <= 1

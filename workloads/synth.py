@@ -522,3 +522,57 @@ def gen_fuzz(seed: int, steps: int = 6) -> Workload:
     return Workload(f"fuzz{seed}", B, Nq, K, S, row_bytes, steps, 1000 + seed,
                     topk, ctx, host_rows, row_base, L=L, R=R, a1=a1, a2=a2,
                     afp=afp)
+
+
+def gen_medium(seed: int, steps: int = 3) -> Workload:
+    """A random medium-sized case across the supported shapes.
+
+    K in 1..4096 with N_q*K <= 8192, N_q in 1..4, S the smallest power of two
+    >= N_q*K times 1, 2 or 4 (at most 16384), B up to 300 (more requests than CUs for small K),
+    lookups per step kept under about 300k so the oracle stays fast.  Each
+    token keeps about half of the request's previous selection and draws the
+    rest fresh; padding, out-of-range ids and ids at or beyond the verified
+    length are mixed in.  Rows are 16 to 64 bytes so the host pool stays small.
+    """
+    rng = np.random.default_rng([9, seed])
+    Nq = int(rng.integers(1, 5))
+    K = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(64, 1025)),
+                        int(rng.integers(1024, 4097))]))
+    K = max(1, min(K, 8192 // Nq))
+    S = 16
+    while S < Nq * K:
+        S *= 2
+    S = min(16384, S * int(rng.choice([1, 2, 4])))
+    B = int(rng.integers(1, max(2, min(300, 300_000 // (Nq * K)) + 1)))
+    L = int(rng.choice([1, 3, 15, 63]))
+    R = int(rng.choice([0, 2, 7, min(15, S - 1)]))
+    host_rows = rng.integers(max(K + 1, 2 * K), 8 * K + 64, size=B).astype(np.int32)
+    topk = np.full((steps, B, Nq, K), -1, np.int32)
+    ctx = np.zeros((steps, B), np.int32)
+    prev = [None] * B
+    for t in range(steps):
+        for b in range(B):
+            hr = int(host_rows[b])
+            ctx[t, b] = int(rng.integers(max(1, (3 * hr) // 4), hr + 1))
+            for g in range(Nq):
+                n = K - int(rng.integers(0, max(1, K // 8) + 1))
+                if prev[b] is not None and prev[b].size:
+                    keep = rng.choice(prev[b], min(prev[b].size, n // 2), replace=False)
+                else:
+                    keep = np.empty(0, np.int64)
+                fresh = np.setdiff1d(rng.choice(hr, min(hr, 2 * n), replace=False), keep)
+                ids = np.concatenate([keep, fresh[: n - keep.size]]).astype(np.int32)
+                prev[b] = ids
+                row = np.full(K, -1, np.int32)
+                row[rng.permutation(K)[: ids.size]] = rng.permutation(ids)
+                if ids.size < K and rng.random() < 0.2:
+                    free = np.flatnonzero(row == -1)
+                    row[free[0]] = int(rng.choice([-7, hr, hr + 11]))
+                topk[t, b, g] = row
+    row_base = np.concatenate([[0], np.cumsum(host_rows)[:-1]]).astype(np.int64)
+    a1 = int(rng.integers(0, 2**31)) * 2 + 1
+    a2 = int(rng.integers(0, 2**31)) * 2 + 1
+    afp = int(rng.integers(0, 2**31)) * 2 + 1
+    row_bytes = int(rng.choice([16, 32, 64]))
+    return Workload(f"medium{seed}", B, Nq, K, S, row_bytes, steps, 2000 + seed,
+                    topk, ctx, host_rows, row_base, L=L, R=R, a1=a1, a2=a2, afp=afp)
