@@ -356,6 +356,27 @@ __device__ inline void link_rounds(const int32_t* sQ, const int32_t* sC, uint32_
     }
 }
 
+// The kernel's arguments as the several-requests form reads its per-request
+// ones (state bases, row tables, counters, B): through a pointer to the
+// argument segment that the compiler cannot follow from one read to the
+// next, so that those values are loaded where a request starts or is loaded
+// ahead instead of being held in scalar registers across the token loop.
+typedef __attribute__((address_space(4))) const Stage1Args ConstArgs;
+
+template <bool MULTI>
+struct RequestArgs {
+    __device__ static const Stage1Args& get(const Stage1Args& a) { return a; }
+};
+
+template <>
+struct RequestArgs<true> {
+    __device__ static ConstArgs& get(const Stage1Args&) {
+        ConstArgs* p = (ConstArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(p));
+        return *p;
+    }
+};
+
 // One staging pass: int4 words j0 + u*T (u < U) of Q, C and F into LDS.
 // Branch-free so that all loads of a pass are in flight together: indices
 // past the end are clamped to the last word, and the threads that clamp
@@ -437,9 +458,10 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
     int32_t xn[IPT];
     for (int b = blockIdx.x;;) {
         const int bn = b + int(gridDim.x);  // this workgroup's next request
-        int32_t* gQ = a.Q + size_t(b) * S;
-        int32_t* gC = a.C + size_t(b) * S;
-        int32_t* gF = a.F + size_t(b) * S;
+        auto& A = RequestArgs<MULTI>::get(a);
+        int32_t* gQ = A.Q + size_t(b) * S;
+        int32_t* gC = A.C + size_t(b) * S;
+        int32_t* gF = A.F + size_t(b) * S;
         int32_t* const mrow = DENSE ? a.map + size_t(b) * size_t(a.map_len) : nullptr;
 
         int64_t rb;
@@ -464,9 +486,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         } else {
             // The request's scalars are read before anything else so that their
             // latency overlaps the staging loads.
-            rb = a.row_base[b];
-            hr = a.host_rows[b];
-            N = a.ctx_len[b];
+            rb = A.row_base[b];
+            hr = A.host_rows[b];
+            N = A.ctx_len[b];
 
             // Stage the request's state.  The once-per-step decay before the
             // first token is fused into the load: G = max(F - 1, -1) + 1,
@@ -477,7 +499,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             // passes of staging are straight-line code, with no loop head that
             // would wait for them.
             load_ids<IPT>(a.topk + size_t(b) * a.Nq * K, i0, K, xn);
-            cnt_old = a.CNT[size_t(b) * 8 + min(tid, 7)];  // used by tid < 8
+            cnt_old = A.CNT[size_t(b) * 8 + min(tid, 7)];  // used by tid < 8
             if (nq <= T) {
                 stage_pass<T, 1, DENSE>(gQ, gC, gF, sQ, sC, sGw, tid, nq, gadd, L);
             } else if (nq <= 2 * T) {
@@ -488,9 +510,9 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             }
         }
         // Whether the next request's state is loaded ahead, during this one.
-        const bool prefetch_next = kPrefetch && bn < a.B && nq <= 2 * T;
+        const bool prefetch_next = kPrefetch && bn < A.B && nq <= 2 * T;
 
-        const bool row_ok = rb >= 0 && hr >= 0 && rb + hr <= a.host_rows_total;
+        const bool row_ok = rb >= 0 && hr >= 0 && rb + hr <= A.host_rows_total;
         // The rank bitmap can cover all of the request's ids.
         const bool narrow_rows = row_ok && hr > 0 && hr <= lay.bitmap_words * 32;
 
@@ -637,9 +659,10 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
             // when this request is done.
             if (g == 0 && prefetch_next) {
                 const int ja = min(tid_t, nq - 1), jb = min(tid_t + T, nq - 1);
-                const int4* nQ = reinterpret_cast<const int4*>(a.Q + size_t(bn) * S);
-                const int4* nC = reinterpret_cast<const int4*>(a.C + size_t(bn) * S);
-                const int4* nF = reinterpret_cast<const int4*>(a.F + size_t(bn) * S);
+                auto& An = RequestArgs<MULTI>::get(a);
+                const int4* nQ = reinterpret_cast<const int4*>(An.Q + size_t(bn) * S);
+                const int4* nC = reinterpret_cast<const int4*>(An.C + size_t(bn) * S);
+                const int4* nF = reinterpret_cast<const int4*>(An.F + size_t(bn) * S);
                 pq0 = nQ[ja];
                 pc0 = nC[ja];
                 pf0 = nF[ja];
@@ -648,10 +671,10 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
                     pc1 = nC[jb];
                     pf1 = nF[jb];
                 }
-                p_rb = a.row_base[bn];
-                p_hr = a.host_rows[bn];
-                p_N = a.ctx_len[bn];
-                p_cnt = a.CNT[size_t(bn) * 8 + min(tid_t, 7)];
+                p_rb = An.row_base[bn];
+                p_hr = An.host_rows[bn];
+                p_N = An.ctx_len[bn];
+                p_cnt = An.CNT[size_t(bn) * 8 + min(tid_t, 7)];
             }
             // open now holds exactly the valid misses.
             const uint32_t missm = open;
@@ -980,7 +1003,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         }
         __syncthreads();
         if (tid < 8) {
-            int32_t* cnt = a.CNT + size_t(b) * 8;
+            int32_t* cnt = RequestArgs<MULTI>::get(a).CNT + size_t(b) * 8;
             const uint32_t add = tid == 0   ? uint32_t(sCnt[1]) - c_miss
                                  : tid == 2 ? c_miss
                                             : uint32_t(sCnt[tid]);
@@ -992,7 +1015,7 @@ __global__ __launch_bounds__(T) void stage1_kernel(Stage1Args a) {
         if constexpr (!MULTI) break;
         have_pre = prefetch_next;
         b = bn;
-        if (b >= a.B) break;
+        if (b >= RequestArgs<MULTI>::get(a).B) break;
     }
 }
 
