@@ -897,13 +897,14 @@ def test_continuation_with_more_requests_than_cus(K, S):
 def test_random_medium_configs(chunk):
     """Random shapes across the supported range (K up to 4096, N_q up to 4,
     S up to 16384, B up to 300, several L and R, random hash multipliers),
-    each with a random matcher or copy partition, workgroup size and with
-    or without the copy: every id-per-thread form, several requests per
-    workgroup, padding, out-of-range and speculative ids, all against the
-    oracle after every step."""
+    each with a random matcher (hash, dense map, sort-merge, no reuse) or
+    copy partition, workgroup size and with or without the copy: every
+    id-per-thread form, several requests per workgroup, padding,
+    out-of-range and speculative ids, all against the oracle after every
+    step."""
     import recall_step_amd as r
     from workloads import gen_medium
-    for seed in range(chunk, 32, 4):
+    for seed in range(chunk, 48, 4):
         w = gen_medium(seed)
         rng = np.random.default_rng([11, seed])
         # The largest S at most the drawn one whose state fits the LDS.
@@ -917,7 +918,10 @@ def test_random_medium_configs(chunk):
             say(f"[parity] medium {seed}: K={w.K} S={w.S} does not fit the LDS; skipped")
             continue
         flags = int(rng.choice([0, 0, r.FLAG_DENSE_MAP, r.FLAG_GATHER_BY_REQUEST,
-                                r.FLAG_GATHER_BY_TOPK]))
+                                r.FLAG_GATHER_BY_TOPK, r.FLAG_SORT_MERGE, r.FLAG_NO_REUSE]))
+        if flags == r.FLAG_SORT_MERGE and r.avsg_stage1_lds_bytes(r.avsg_config_default(
+                w.B, w.Nq, w.K, w.S, w.row_bytes, flags=flags)) == 0:
+            flags = 0  # the sort-merge matcher's keys do not fit the LDS at this S
         threads = int(rng.choice([0] + [t for t in (256, 512, 1024) if w.K <= 8 * t]))
         gather = bool(rng.random() < 0.75)
         run_parity(w, kv_every=1, gather=gather, flags=flags, stage1_threads=threads,
