@@ -30,7 +30,9 @@
 // (ascending id), installs them into the victim of that rank and writes its
 // slot-table and hit-mask entries with vector stores.  The install leaves the
 // misses in rank order in LDS, and the link runs over that list, one miss per
-// lane, so only as many waves as there are misses walk its rounds.  The rank
+// lane (more only where a token has more misses than threads), so only as
+// many waves as there are misses walk its rounds, each over just the ids its
+// lanes hold: a round lasts one wave's chain of dependent instructions.  The rank
 // comes from a bitmap held in LDS over [0, host rows) of the request (or, if
 // those do not fit it, over [min id, max id] of the token's misses): one
 // atomicOr per miss, then prefix popcounts over the words, so rank(x) =
